@@ -1,0 +1,190 @@
+/*
+ * moe.h -- C ABI of the single-GPU Mixture-of-Experts feed-forward layer
+ * (forward pass) for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (chapter "大模型推理技术 | 第11章 MoE模型推理", jsqmd.com,
+ * sections 11.1.1-11.1.2):
+ *     y = sum over the K chosen experts i of  gate_i(x) * E_i(x)
+ *     E_i(x) = GeLU(x W1_i + b1_i) W2_i + b2_i        (exact erf GeLU)
+ *     gates  = softmax of the router scores x W_r (+ router_bias) over the
+ *              K experts with the largest scores (renormalize = 1), or their
+ *              full-softmax probabilities (renormalize = 0).
+ * Optional DeepSeek-V3 style selection ("MoE 推理工程深层实战", ybb.press,
+ * section 2.3): a per-expert select_bias is added to the scores for selection
+ * only, and with n_groups > 1 the experts are split into n_groups groups of
+ * consecutive experts; only the topk_groups groups with the largest summed
+ * biased score stay eligible.
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE pointers, row-major, 16-byte aligned, owned by
+ *    the caller.  The library keeps no pointer after a call returns.
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL = the
+ *    default stream).  No call synchronises the host, reads device data back,
+ *    or allocates memory.  Buffers must stay alive until the stream reaches
+ *    the work.
+ *  - Arguments are validated on the host before anything is launched.  On a
+ *    validation failure the call returns a negative moe_status and writes
+ *    nothing.  A failed kernel launch returns MOE_ERR_HIP.  Nothing aborts and
+ *    no C++ exception crosses the ABI.
+ *  - S == 0 is a no-op that returns MOE_OK (pointers may then be NULL).
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *    Different calls may run concurrently only on distinct buffers.
+ *  - Inputs are finite numbers; NaN or Inf inputs are outside the contract.
+ *
+ * Data types (moe_problem.act_dtype / w_dtype)
+ *  - act: x, W_r, b1, b2, x_perm, h, y_perm, y          MOE_F32 or MOE_BF16
+ *  - w:   W1, W2    MOE_F32 (with act F32), MOE_BF16 or MOE_FP8_E4M3 (with
+ *         act BF16).  fp8 is OCP E4M3FN; the weight value is
+ *         decode(code) * scale[e][output channel].
+ *  - logits, gates, router_bias, select_bias, scales: float32
+ *  - indices, counts, offsets, perm, inv_perm: int32
+ *
+ * Weight layout: each matrix is stored like a linear layer's weight,
+ * [out_features, in_features], so the contraction index is contiguous:
+ *     W_r [E][d]    W1 [E][d_ff][d]    W2 [E][d][d_ff]
+ *     b1 [E][d_ff]  b2 [E][d]          w1_scale [E][d_ff]   w2_scale [E][d]
+ * (x W1 in the pages' notation is x times the transpose of the stored W1.)
+ */
+#ifndef SPARSE_FFN_LAYER_MOE_H
+#define SPARSE_FFN_LAYER_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* bad shape, NULL or misaligned pointer, bad flag */
+  MOE_ERR_UNSUPPORTED = -2, /* valid problem outside what the kernels handle */
+  MOE_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than required */
+  MOE_ERR_HIP = -4          /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Which entry point a workspace is sized for. */
+typedef enum {
+  MOE_STAGE_ROUTE = 0,
+  MOE_STAGE_PERMUTE = 1,
+  MOE_STAGE_EXPERT_FFN = 2,
+  MOE_STAGE_COMBINE = 3,
+  MOE_STAGE_LAYER = 4
+} moe_stage;
+
+/* The problem statement: S tokens of width d (S = batch x sequence, chapter
+ * 11 section 11.3.1), E experts with hidden width d_ff, K experts per token.
+ *  - n_groups <= 1: no group limit.  Otherwise E % n_groups == 0, E/n_groups
+ *    a power of two, n_groups <= 64, 1 <= topk_groups <= n_groups and
+ *    K <= topk_groups * E / n_groups.
+ *  - renormalize: 1 = gates are the softmax over the K chosen scores (sum to
+ *    1); 0 = gates are the chosen experts' full-softmax probabilities.
+ *  - Limits: 1 <= E <= 512, 1 <= K <= min(E, 64), d and d_ff multiples of 64,
+ *    S < 2^31 / K.  Outside them: MOE_ERR_UNSUPPORTED. */
+typedef struct {
+  int64_t S;
+  int32_t d;
+  int32_t d_ff;
+  int32_t E;
+  int32_t K;
+  int32_t n_groups;
+  int32_t topk_groups;
+  int32_t renormalize;
+  int32_t act_dtype; /* moe_dtype */
+  int32_t w_dtype;   /* moe_dtype */
+} moe_problem;
+
+/* Host-only, pure helpers (no HIP call).  They return 0 / -1 for a problem
+ * that fails validation. */
+
+/* Bytes of device workspace the entry point `stage` needs for `p`. */
+size_t moe_workspace_bytes(const moe_problem* p, int32_t stage);
+
+/* Padding granule of the expert-contiguous buffers (x_perm, h, y_perm): each
+ * expert's group of rows starts at a multiple of it. */
+int32_t moe_tile_m(const moe_problem* p);
+
+/* Rows x_perm, h and y_perm must hold: S*K + min(E, S*K) * (tile_m - 1). */
+int64_t moe_rows_capacity(const moe_problem* p);
+
+/* Static text for a status code. */
+const char* moe_status_string(int32_t status);
+
+/* Router and Top-K selection (chapter 11 sections 11.1.1-11.1.2; selection
+ * bias and group limit: ybb.press section 2.3; one MoE forward and the
+ * worked example: "MoE 混合专家推理", plumephp.com).
+ *   x [S][d] act, W_r [E][d] act
+ *   router_bias [E] (nullable): added to the scores; enters the gates.
+ *   select_bias [E] (nullable): added to the scores for selection only.
+ *   logits_in [S][E] (nullable): use these float32 scores instead of x W_r;
+ *       x and W_r may then be NULL.  router_bias is not added to them.
+ *   logits_out [S][E] (nullable): receives the float32 scores.
+ *   topk_idx [S][K]: chosen experts per token, in slot order: key
+ *       (score + select_bias) descending, equal keys by lower expert index.
+ *   topk_gate [S][K]: float32 gate of each slot.
+ *   ws: moe_workspace_bytes(p, MOE_STAGE_ROUTE) bytes (may be 0). */
+int32_t moe_route(const moe_problem* p, const void* x, const void* W_r,
+                  const float* router_bias, const float* select_bias,
+                  const float* logits_in, float* logits_out,
+                  int32_t* topk_idx, float* topk_gate,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch: regroup the S*K (token, slot) pairs per expert (chapter 11
+ * section 11.2.1).  Pair id = t*K + k.  Within an expert pairs keep token
+ * order.
+ *   topk_idx [S][K] int32 in [0, E) with distinct entries per token.
+ *   expert_counts [E]: pairs routed to each expert.
+ *   expert_offsets [E+1]: first padded row of each expert's group; every
+ *       entry is a multiple of moe_tile_m(p); entry E is the rows used.
+ *   perm [S*K]: pair ids in (expert, token) order (no padding).
+ *   inv_perm [S*K]: padded row of each pair.
+ *   x_perm [moe_rows_capacity(p)][d] act: x_perm[inv_perm[t*K+k]] = x[t];
+ *       padding rows are left untouched.
+ *   ws: moe_workspace_bytes(p, MOE_STAGE_PERMUTE) bytes. */
+int32_t moe_permute(const moe_problem* p, const int32_t* topk_idx, const void* x,
+                    int32_t* expert_counts, int32_t* expert_offsets,
+                    int32_t* perm, int32_t* inv_perm, void* x_perm,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFN as a grouped GEMM over the expert-contiguous rows (chapter 11
+ * section 11.1.2): for each real row r of expert e,
+ *   h[r]      = GeLU(x_perm[r] W1_e + b1_e)   (act dtype; bf16 rounds once)
+ *   y_perm[r] = h[r] W2_e + b2_e             (act dtype)
+ * Padding rows of h and y_perm are unspecified.  Experts with no rows read
+ * no weights.
+ *   expert_counts, expert_offsets: as produced by moe_permute for this p.
+ *   w1_scale, w2_scale: required for MOE_FP8_E4M3 weights, else ignored.
+ *   h [rows_capacity][d_ff], y_perm [rows_capacity][d].
+ *   ws: moe_workspace_bytes(p, MOE_STAGE_EXPERT_FFN) bytes (may be 0). */
+int32_t moe_expert_ffn(const moe_problem* p, const void* x_perm,
+                       const int32_t* expert_counts, const int32_t* expert_offsets,
+                       const void* W1, const void* b1, const void* W2, const void* b2,
+                       const float* w1_scale, const float* w2_scale,
+                       void* h, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine (chapter 11 sections 11.1.1 and 11.2.1; "MoE 混合专家推理", one
+ * MoE forward): y[t] = sum over k = 0..K-1, in slot order, of
+ * topk_gate[t][k] * y_perm[inv_perm[t*K+k]], accumulated in float32 and
+ * rounded once to the act dtype.  No atomics. */
+int32_t moe_combine(const moe_problem* p, const void* y_perm, const int32_t* inv_perm,
+                    const float* topk_gate, void* y, void* stream);
+
+/* The whole layer: route, permute, expert FFN, combine on one stream.
+ *   y [S][d] act.  Optional outputs (nullable): topk_idx_out [S][K],
+ *   topk_gate_out [S][K], logits_out [S][E], expert_counts_out [E].
+ *   ws: moe_workspace_bytes(p, MOE_STAGE_LAYER) bytes. */
+int32_t moe_layer_forward(const moe_problem* p, const void* x, const void* W_r,
+                          const float* router_bias, const float* select_bias,
+                          const void* W1, const void* b1, const void* W2, const void* b2,
+                          const float* w1_scale, const float* w2_scale, void* y,
+                          int32_t* topk_idx_out, float* topk_gate_out,
+                          float* logits_out, int32_t* expert_counts_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_FFN_LAYER_MOE_H */

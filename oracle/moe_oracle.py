@@ -63,7 +63,7 @@ def decode_bf16(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
+def _e4m3fn_value(c: np.ndarray) -> np.ndarray:
     """OCP 8-bit floating point E4M3 ('fn': finite, no infinities) -> float64.
 
     Sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0.  Exponent
@@ -71,13 +71,22 @@ def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
     pattern S.1111.111 is NaN; there is no infinity, so the largest finite
     magnitude is 1.75 * 2^8 = 448.
     """
-    c = np.asarray(codes).astype(np.int64)
+    c = np.asarray(c).astype(np.int64)
     s = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = (c & 0x7).astype(np.float64)
     val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
     val = s * val
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+_E4M3FN_TABLE = _e4m3fn_value(np.arange(256))
+
+
+def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
+    """e4m3fn codes (uint8) -> float64 by the definition above, evaluated
+    once for all 256 codes and looked up."""
+    return _E4M3FN_TABLE[np.asarray(codes).astype(np.uint8)]
 
 
 def decode(arr: np.ndarray, dtype: str) -> np.ndarray:

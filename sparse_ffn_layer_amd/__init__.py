@@ -1,0 +1,205 @@
+"""Python binding of the MoE-layer C ABI (include/moe.h) for MI355X.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+of libsfl_moe.so.  torch provides device memory and the current stream.
+There is no CPU or pure-PyTorch fallback: if the library is missing, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
+    "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "STAGE_ROUTE", "STAGE_PERMUTE", "STAGE_EXPERT_FFN",
+    "STAGE_COMBINE", "STAGE_LAYER", "MoEError", "moe_problem", "make_problem", "lib", "LIB_PATH",
+    "moe_workspace_bytes", "moe_tile_m", "moe_rows_capacity", "moe_status_string",
+    "workspace", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfl_moe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+STAGE_ROUTE, STAGE_PERMUTE, STAGE_EXPERT_FFN, STAGE_COMBINE, STAGE_LAYER = 0, 1, 2, 3, 4
+
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3,
+       torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3}
+_ACT_TORCH = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({moe_status_string(status)})")
+        self.status = status
+
+
+class moe_problem(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int64), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32)]
+
+
+def make_problem(S, d, d_ff, E, K, act="bf16", w="bf16", n_groups=1, topk_groups=1,
+                 renormalize=1) -> moe_problem:
+    return moe_problem(int(S), int(d), int(d_ff), int(E), int(K), int(n_groups), int(topk_groups),
+                       int(renormalize), _DT[act], _DT[w])
+
+
+_lib = None
+_P = ctypes.POINTER(moe_problem)
+_vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+
+_SIGS = {
+    "moe_workspace_bytes": (_sz, [_P, _i32]),
+    "moe_tile_m": (_i32, [_P]),
+    "moe_rows_capacity": (_i64, [_P]),
+    "moe_status_string": (ctypes.c_char_p, [_i32]),
+    "moe_route": (_i32, [_P] + [_vp] * 8 + [_vp, _sz, _vp]),
+    "moe_permute": (_i32, [_P] + [_vp] * 7 + [_vp, _sz, _vp]),
+    "moe_expert_ffn": (_i32, [_P] + [_vp] * 11 + [_vp, _sz, _vp]),
+    "moe_combine": (_i32, [_P] + [_vp] * 4 + [_vp]),
+    "moe_layer_forward": (_i32, [_P] + [_vp] * 15 + [_vp, _sz, _vp]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sparse_ffn_layer_amd.build` (hipcc, gfx950)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype, f.argtypes = res, args
+        _lib = l
+    return _lib
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream or None
+    return getattr(stream, "cuda_stream", stream) or None
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def moe_workspace_bytes(p: moe_problem, stage: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(p), int(stage)))
+
+
+def moe_tile_m(p: moe_problem) -> int:
+    return int(lib().moe_tile_m(ctypes.byref(p)))
+
+
+def moe_rows_capacity(p: moe_problem) -> int:
+    return int(lib().moe_rows_capacity(ctypes.byref(p)))
+
+
+def workspace(p: moe_problem, stage: int, device="cuda") -> torch.Tensor:
+    n = moe_workspace_bytes(p, stage)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def _act(p: moe_problem):
+    return _ACT_TORCH[p.act_dtype]
+
+
+# ------------------------------------------------------------------ entry points
+def moe_route(p, x, W_r, router_bias=None, select_bias=None, logits_in=None, logits_out=None,
+              topk_idx=None, topk_gate=None, ws=None, stream=None):
+    dev = (logits_in if logits_in is not None else x).device
+    if topk_idx is None:
+        topk_idx = torch.empty((p.S, p.K), dtype=torch.int32, device=dev)
+    if topk_gate is None:
+        topk_gate = torch.empty((p.S, p.K), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(p, STAGE_ROUTE, dev)
+    st = lib().moe_route(ctypes.byref(p), _ptr(x), _ptr(W_r), _ptr(router_bias), _ptr(select_bias),
+                         _ptr(logits_in), _ptr(logits_out), _ptr(topk_idx), _ptr(topk_gate),
+                         _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_route", st)
+    return topk_idx, topk_gate
+
+
+def moe_permute(p, topk_idx, x, expert_counts=None, expert_offsets=None, perm=None, inv_perm=None,
+                x_perm=None, ws=None, stream=None):
+    dev = topk_idx.device
+    pairs = p.S * p.K
+    i32 = dict(dtype=torch.int32, device=dev)
+    expert_counts = torch.empty(p.E, **i32) if expert_counts is None else expert_counts
+    expert_offsets = torch.empty(p.E + 1, **i32) if expert_offsets is None else expert_offsets
+    perm = torch.empty(pairs, **i32) if perm is None else perm
+    inv_perm = torch.empty(pairs, **i32) if inv_perm is None else inv_perm
+    if x_perm is None:
+        x_perm = torch.empty((moe_rows_capacity(p), p.d), dtype=_act(p), device=dev)
+    if ws is None:
+        ws = workspace(p, STAGE_PERMUTE, dev)
+    st = lib().moe_permute(ctypes.byref(p), _ptr(topk_idx), _ptr(x), _ptr(expert_counts),
+                           _ptr(expert_offsets), _ptr(perm), _ptr(inv_perm), _ptr(x_perm),
+                           _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_permute", st)
+    return expert_counts, expert_offsets, perm, inv_perm, x_perm
+
+
+def moe_expert_ffn(p, x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, w1_scale=None,
+                   w2_scale=None, h=None, y_perm=None, ws=None, stream=None):
+    dev = x_perm.device
+    cap = moe_rows_capacity(p)
+    h = torch.empty((cap, p.d_ff), dtype=_act(p), device=dev) if h is None else h
+    y_perm = torch.empty((cap, p.d), dtype=_act(p), device=dev) if y_perm is None else y_perm
+    if ws is None:
+        ws = workspace(p, STAGE_EXPERT_FFN, dev)
+    st = lib().moe_expert_ffn(ctypes.byref(p), _ptr(x_perm), _ptr(expert_counts), _ptr(expert_offsets),
+                              _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(w1_scale), _ptr(w2_scale),
+                              _ptr(h), _ptr(y_perm), _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_expert_ffn", st)
+    return h, y_perm
+
+
+def moe_combine(p, y_perm, inv_perm, topk_gate, y=None, stream=None):
+    if y is None:
+        y = torch.empty((p.S, p.d), dtype=_act(p), device=y_perm.device)
+    st = lib().moe_combine(ctypes.byref(p), _ptr(y_perm), _ptr(inv_perm), _ptr(topk_gate), _ptr(y),
+                           _stream(stream))
+    _check("moe_combine", st)
+    return y
+
+
+def moe_layer_forward(p, x, W_r, W1, b1, W2, b2, router_bias=None, select_bias=None, w1_scale=None,
+                      w2_scale=None, y=None, topk_idx_out=None, topk_gate_out=None, logits_out=None,
+                      expert_counts_out=None, ws=None, stream=None):
+    if y is None:
+        y = torch.empty((p.S, p.d), dtype=_act(p), device=x.device)
+    if ws is None:
+        ws = workspace(p, STAGE_LAYER, x.device)
+    st = lib().moe_layer_forward(ctypes.byref(p), _ptr(x), _ptr(W_r), _ptr(router_bias),
+                                 _ptr(select_bias), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                                 _ptr(w1_scale), _ptr(w2_scale), _ptr(y), _ptr(topk_idx_out),
+                                 _ptr(topk_gate_out), _ptr(logits_out), _ptr(expert_counts_out),
+                                 _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_layer_forward", st)
+    return y

@@ -1,0 +1,270 @@
+// C ABI of the MoE layer: argument validation, workspace layout and launch
+// order.  Everything here runs on the host; validation happens before any HIP
+// call, so invalid arguments are reported without touching a device.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace sfl {
+// kernels (router.hip, permute.hip, gemm.hip, combine.hip)
+hipError_t launch_router_fused(const Problem&, const void*, const void*, const float*,
+                               const float*, float*, int32_t*, float*, hipStream_t);
+hipError_t launch_route_logits(const Problem&, const float*, const float*, float*, int32_t*,
+                               float*, hipStream_t);
+hipError_t launch_router_gemm(const Problem&, const void*, const void*, const float*, float*,
+                              hipStream_t);
+hipError_t launch_permute(const Problem&, int, const int32_t*, const void*, int32_t*, int32_t*,
+                          int32_t*, int32_t*, void*, int32_t*, hipStream_t);
+size_t permute_scratch_ints(int64_t pairs, int E);
+hipError_t launch_expert_ffn(const Problem&, int64_t, const void*, const int32_t*,
+                             const int32_t*, const void*, const void*, const void*, const void*,
+                             const float*, const float*, void*, void*, hipStream_t);
+hipError_t launch_combine(const Problem&, const void*, const int32_t*, const float*, void*,
+                          hipStream_t);
+int gemm_tile_m(const Problem& p);
+}  // namespace sfl
+
+using namespace sfl;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Validate the problem statement itself (no pointers).
+int32_t check_problem(const moe_problem* mp, Problem* out) {
+  if (mp == nullptr) return MOE_ERR_INVALID_ARG;
+  const moe_problem& q = *mp;
+  if (q.S < 0 || q.d < 1 || q.d_ff < 1 || q.E < 1 || q.K < 1 || q.K > q.E)
+    return MOE_ERR_INVALID_ARG;
+  if (q.renormalize != 0 && q.renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (q.act_dtype < MOE_F32 || q.act_dtype > MOE_FP8_E4M3 || q.w_dtype < MOE_F32 ||
+      q.w_dtype > MOE_FP8_E4M3)
+    return MOE_ERR_INVALID_ARG;
+  if (q.n_groups > 1) {
+    if (q.E % q.n_groups != 0) return MOE_ERR_INVALID_ARG;
+    const int m = q.E / q.n_groups;
+    if ((m & (m - 1)) != 0) return MOE_ERR_INVALID_ARG;
+    if (q.topk_groups < 1 || q.topk_groups > q.n_groups) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)q.K > (int64_t)q.topk_groups * m) return MOE_ERR_INVALID_ARG;
+    if (q.n_groups > 64) return MOE_ERR_UNSUPPORTED;
+  }
+  const bool combo = (q.act_dtype == MOE_F32 && q.w_dtype == MOE_F32) ||
+                     (q.act_dtype == MOE_BF16 && (q.w_dtype == MOE_BF16 || q.w_dtype == MOE_FP8_E4M3));
+  if (!combo) return MOE_ERR_UNSUPPORTED;
+  if (q.E > 512 || q.K > 64 || q.d % 64 != 0 || q.d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (q.S > 0 && q.S >= (int64_t)(INT32_MAX / 2) / q.K) return MOE_ERR_UNSUPPORTED;
+  if (out != nullptr) {
+    out->S = q.S; out->d = q.d; out->d_ff = q.d_ff; out->E = q.E; out->K = q.K;
+    out->n_groups = q.n_groups > 1 ? q.n_groups : 1;
+    out->topk_groups = q.n_groups > 1 ? q.topk_groups : 1;
+    out->renormalize = q.renormalize; out->act = q.act_dtype; out->w = q.w_dtype;
+  }
+  return MOE_OK;
+}
+
+bool uses_router_gemm(const Problem& p) { return p.act == DT_BF16 && p.E >= 64 && p.E % 64 == 0; }
+
+size_t act_size(const Problem& p) { return p.act == DT_F32 ? 4 : 2; }
+
+int64_t rows_capacity(const Problem& p) {
+  const int64_t pairs = p.S * p.K;
+  const int64_t tm = gemm_tile_m(p);
+  return pairs + (pairs < p.E ? pairs : p.E) * (tm - 1);
+}
+
+size_t route_ws(const Problem& p) { return uses_router_gemm(p) ? align_up((size_t)p.S * p.E * 4) : 0; }
+size_t permute_ws(const Problem& p) { return align_up(permute_scratch_ints(p.S * p.K, p.E) * 4); }
+
+// Layout of the layer workspace: consecutive 256-byte aligned regions.
+struct LayerWs {
+  float* logits; int32_t* idx; float* gate; int32_t* counts; int32_t* offsets;
+  int32_t* perm; int32_t* inv; int32_t* pscratch; void* x_perm; void* h; void* y_perm;
+  size_t bytes;
+};
+LayerWs layer_layout(const Problem& p, char* base) {
+  LayerWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* ptr = base ? base + off : nullptr; off += align_up(bytes); return ptr; };
+  const int64_t pairs = p.S * p.K, cap = rows_capacity(p);
+  w.logits = (float*)take((size_t)p.S * p.E * 4);
+  w.idx = (int32_t*)take((size_t)pairs * 4);
+  w.gate = (float*)take((size_t)pairs * 4);
+  w.counts = (int32_t*)take((size_t)p.E * 4);
+  w.offsets = (int32_t*)take((size_t)(p.E + 1) * 4);
+  w.perm = (int32_t*)take((size_t)pairs * 4);
+  w.inv = (int32_t*)take((size_t)pairs * 4);
+  w.pscratch = (int32_t*)take(permute_scratch_ints(pairs, p.E) * 4);
+  w.x_perm = take((size_t)cap * p.d * act_size(p));
+  w.h = take((size_t)cap * p.d_ff * act_size(p));
+  w.y_perm = take((size_t)cap * p.d * act_size(p));
+  w.bytes = off;
+  return w;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int32_t do_route(const Problem& p, const void* x, const void* Wr, const float* rb, const float* sb,
+                 const float* logits_in, float* logits_out, int32_t* idx, float* gate,
+                 float* logits_scratch, hipStream_t st) {
+  if (logits_in != nullptr)
+    return hip_status(launch_route_logits(p, logits_in, sb, logits_out, idx, gate, st));
+  if (uses_router_gemm(p)) {
+    float* lg = logits_out != nullptr ? logits_out : logits_scratch;
+    hipError_t e = launch_router_gemm(p, x, Wr, rb, lg, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_route_logits(p, lg, sb, nullptr, idx, gate, st));
+  }
+  return hip_status(launch_router_fused(p, x, Wr, rb, sb, logits_out, idx, gate, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported problem";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_tile_m(const moe_problem* mp) {
+  Problem p;
+  if (check_problem(mp, &p) != MOE_OK) return -1;
+  return gemm_tile_m(p);
+}
+
+int64_t moe_rows_capacity(const moe_problem* mp) {
+  Problem p;
+  if (check_problem(mp, &p) != MOE_OK) return -1;
+  return rows_capacity(p);
+}
+
+size_t moe_workspace_bytes(const moe_problem* mp, int32_t stage) {
+  Problem p;
+  if (check_problem(mp, &p) != MOE_OK) return 0;
+  switch (stage) {
+    case MOE_STAGE_ROUTE: return route_ws(p);
+    case MOE_STAGE_PERMUTE: return permute_ws(p);
+    case MOE_STAGE_EXPERT_FFN: return 0;
+    case MOE_STAGE_COMBINE: return 0;
+    case MOE_STAGE_LAYER: return layer_layout(p, nullptr).bytes;
+    default: return 0;
+  }
+}
+
+int32_t moe_route(const moe_problem* mp, const void* x, const void* W_r, const float* router_bias,
+                  const float* select_bias, const float* logits_in, float* logits_out,
+                  int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
+  Problem p;
+  int32_t s = check_problem(mp, &p);
+  if (s != MOE_OK) return s;
+  if (p.S == 0) return MOE_OK;
+  if (topk_idx == nullptr || topk_gate == nullptr) return MOE_ERR_INVALID_ARG;
+  if (logits_in == nullptr && (x == nullptr || W_r == nullptr)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, W_r, router_bias, select_bias, logits_in, logits_out, topk_idx, topk_gate};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return MOE_ERR_INVALID_ARG;
+  const size_t need = (logits_in == nullptr && logits_out == nullptr) ? route_ws(p) : 0;
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  return do_route(p, x, W_r, router_bias, select_bias, logits_in, logits_out, topk_idx, topk_gate,
+                  (float*)ws, (hipStream_t)stream);
+}
+
+int32_t moe_permute(const moe_problem* mp, const int32_t* topk_idx, const void* x,
+                    int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                    int32_t* inv_perm, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  Problem p;
+  int32_t s = check_problem(mp, &p);
+  if (s != MOE_OK) return s;
+  if (p.S == 0) return MOE_OK;
+  const void* ptrs[] = {topk_idx, x, expert_counts, expert_offsets, perm, inv_perm, x_perm};
+  for (const void* q : ptrs)
+    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (ws == nullptr || ws_bytes < permute_ws(p)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_permute(p, gemm_tile_m(p), topk_idx, x, expert_counts, expert_offsets,
+                                   perm, inv_perm, x_perm, (int32_t*)ws, (hipStream_t)stream));
+}
+
+int32_t moe_expert_ffn(const moe_problem* mp, const void* x_perm, const int32_t* expert_counts,
+                       const int32_t* expert_offsets, const void* W1, const void* b1,
+                       const void* W2, const void* b2, const float* w1_scale,
+                       const float* w2_scale, void* h, void* y_perm, void* ws, size_t ws_bytes,
+                       void* stream) {
+  (void)ws; (void)ws_bytes;
+  Problem p;
+  int32_t s = check_problem(mp, &p);
+  if (s != MOE_OK) return s;
+  if (p.S == 0) return MOE_OK;
+  const void* ptrs[] = {x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, h, y_perm};
+  for (const void* q : ptrs)
+    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (p.w == DT_FP8 && (w1_scale == nullptr || w2_scale == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w1_scale) || !aligned16(w2_scale)) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = p.w == DT_FP8;
+  return hip_status(launch_expert_ffn(p, rows_capacity(p), x_perm, expert_counts, expert_offsets,
+                                      W1, b1, W2, b2, fp8 ? w1_scale : nullptr,
+                                      fp8 ? w2_scale : nullptr, h, y_perm, (hipStream_t)stream));
+}
+
+int32_t moe_combine(const moe_problem* mp, const void* y_perm, const int32_t* inv_perm,
+                    const float* topk_gate, void* y, void* stream) {
+  Problem p;
+  int32_t s = check_problem(mp, &p);
+  if (s != MOE_OK) return s;
+  if (p.S == 0) return MOE_OK;
+  const void* ptrs[] = {y_perm, inv_perm, topk_gate, y};
+  for (const void* q : ptrs)
+    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(p, y_perm, inv_perm, topk_gate, y, (hipStream_t)stream));
+}
+
+int32_t moe_layer_forward(const moe_problem* mp, const void* x, const void* W_r,
+                          const float* router_bias, const float* select_bias, const void* W1,
+                          const void* b1, const void* W2, const void* b2, const float* w1_scale,
+                          const float* w2_scale, void* y, int32_t* topk_idx_out,
+                          float* topk_gate_out, float* logits_out, int32_t* expert_counts_out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  Problem p;
+  int32_t s = check_problem(mp, &p);
+  if (s != MOE_OK) return s;
+  if (p.S == 0) return MOE_OK;
+  const void* req[] = {x, W_r, W1, b1, W2, b2, y};
+  for (const void* q : req)
+    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  const void* opt[] = {router_bias, select_bias, w1_scale, w2_scale, topk_idx_out, topk_gate_out,
+                       logits_out, expert_counts_out};
+  for (const void* q : opt)
+    if (!aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (p.w == DT_FP8 && (w1_scale == nullptr || w2_scale == nullptr)) return MOE_ERR_INVALID_ARG;
+  const LayerWs need = layer_layout(p, nullptr);
+  if (ws == nullptr || ws_bytes < need.bytes) return MOE_ERR_WORKSPACE;
+
+  const LayerWs w = layer_layout(p, (char*)ws);
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* idx = topk_idx_out != nullptr ? topk_idx_out : w.idx;
+  float* gate = topk_gate_out != nullptr ? topk_gate_out : w.gate;
+  int32_t* counts = expert_counts_out != nullptr ? expert_counts_out : w.counts;
+  s = do_route(p, x, W_r, router_bias, select_bias, nullptr, logits_out, idx, gate, w.logits, st);
+  if (s != MOE_OK) return s;
+  s = hip_status(launch_permute(p, gemm_tile_m(p), idx, x, counts, w.offsets, w.perm, w.inv,
+                                w.x_perm, w.pscratch, st));
+  if (s != MOE_OK) return s;
+  const bool fp8 = p.w == DT_FP8;
+  s = hip_status(launch_expert_ffn(p, rows_capacity(p), w.x_perm, counts, w.offsets, W1, b1, W2, b2,
+                                   fp8 ? w1_scale : nullptr, fp8 ? w2_scale : nullptr, w.h, w.y_perm,
+                                   st));
+  if (s != MOE_OK) return s;
+  return hip_status(launch_combine(p, w.y_perm, w.inv, gate, y, st));
+}
+
+}  // extern "C"

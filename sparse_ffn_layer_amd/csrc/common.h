@@ -1,0 +1,88 @@
+// Internal helpers shared by the HIP kernels of the MoE layer (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfl {
+
+// ------------------------------------------------------------------ problem
+struct Problem {
+  int64_t S;
+  int d, d_ff, E, K;
+  int n_groups, topk_groups, renormalize;
+  int act, w;  // moe_dtype values
+};
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }
+
+// ------------------------------------------------------------------ types
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// Round-to-nearest-even float -> bfloat16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// exact GeLU: x * Phi(x) = x/2 * (1 + erf(x / sqrt 2))
+__device__ __forceinline__ float gelu_erf(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+// ------------------------------------------------------------------ waves
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// (value desc, index asc) arg-max over the wave; every lane gets the winner.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    float ov = __shfl_xor(v, o, 64);
+    int oi = __shfl_xor(i, o, 64);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+}
+
+// ------------------------------------------------------------------ sync
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that orders LDS traffic but does not drain global loads.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16-byte global -> LDS copy through the load path (no VGPR staging).  Lane i
+// of the wave writes LDS bytes [lds_base + 16 i, lds_base + 16 i + 16); the
+// LDS base must be the same for every lane of the wave.
+__device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+}  // namespace sfl

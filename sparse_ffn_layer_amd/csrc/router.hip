@@ -1,0 +1,281 @@
+// Router: scores, (group-limited) Top-K selection and gates, one wavefront
+// per token.
+//
+// Chapter "大模型推理技术 | 第11章 MoE模型推理" (jsqmd.com), sections
+// 11.1.1-11.1.2: router scores are x W_r, a softmax over the experts gives the
+// routing distribution, TopK keeps the K largest scores.  Section 11.4.1 notes
+// that fusing softmax, Top-K and the weighting into one kernel cuts
+// batch-size-1 latency; here scores, selection and gates share one launch
+// (the weighting itself has to wait for the experts, in the combine kernel).
+// "MoE 推理工程深层实战" (ybb.press), section 2.3: the selection-only bias and
+// the node(group)-limited two-stage choice.
+//
+// Register layout: expert e lives in lane (e % 64), slot (e / 64) of a
+// per-lane array, so a token's E scores sit in registers and every reduction
+// is a wave shuffle.  Ties: equal keys choose the lower expert index, equal
+// group scores the lower group index.  Group scores are float32 sums taken in
+// the pairwise-halving order v[j] += v[j + w], w = m/2 ... 1, over the
+// group's experts in index order.
+#include "common.h"
+
+namespace sfl {
+
+constexpr int ROUTER_WAVES = 4;  // tokens per 256-thread block
+
+// Select K experts from this token's logits and write indices and gates.
+// lg[r]: unbiased logit of expert r*64 + lane (-inf where that is >= E).
+template <int R>
+__device__ __forceinline__ void select_and_gate(const float (&lg)[R], int E, int K,
+                                                const float* __restrict__ sbias, int n_groups,
+                                                int topk_groups, int renorm, int64_t t,
+                                                int32_t* __restrict__ idx_out,
+                                                float* __restrict__ gate_out) {
+  const int lane = lane_id();
+  float key[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = r * 64 + lane;
+    key[r] = lg[r];
+    if (sbias != nullptr && e < E) key[r] = lg[r] + sbias[e];
+  }
+
+  if (n_groups > 1) {
+    const int m = E / n_groups;  // power of two
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = key[r];
+    // pairwise-halving tree inside each group of m consecutive experts
+    for (int w = m >> 1; w >= 1; w >>= 1) {
+      if (w >= 64) {  // partner lives in register r + w/64 of the same lane
+        const int dr = w >> 6, per = m >> 6;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+          for (int s = 1; s < R; ++s) {
+            if (s == dr && r + s < R && (r % per) < dr) v[r] = v[r] + v[r + s];
+          }
+        }
+      } else {  // partner is lane + w of the same register
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float o = __shfl_down(v[r], w, 64);
+          v[r] = v[r] + o;
+        }
+      }
+    }
+    // group heads hold the scores; pick topk_groups groups
+    uint64_t chosen = 0;
+    for (int gk = 0; gk < topk_groups; ++gk) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int e = r * 64 + lane;
+        const int g = e / m;
+        if (e < E && (e % m) == 0 && !((chosen >> g) & 1ull)) {
+          if (v[r] > bv || (v[r] == bv && g < bi)) { bv = v[r]; bi = g; }
+        }
+      }
+      wave_argmax(bv, bi);
+      chosen |= 1ull << bi;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = r * 64 + lane;
+      if (e < E && !((chosen >> (e / m)) & 1ull)) key[r] = -INFINITY;
+    }
+  }
+
+  // K rounds of wave arg-max; lane k keeps slot k's expert and logit
+  int my_e = 0;
+  float my_l = -INFINITY;
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = r * 64 + lane;
+      if (e < E && (key[r] > bv || (key[r] == bv && e < bi))) { bv = key[r]; bi = e; }
+    }
+    wave_argmax(bv, bi);
+    float l_sel = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if ((bi >> 6) == r) {
+        l_sel = lg[r];
+        if ((bi & 63) == lane) key[r] = -INFINITY;  // taken
+      }
+    }
+    l_sel = __shfl(l_sel, bi & 63, 64);
+    if (lane == k) { my_e = bi; my_l = l_sel; }
+  }
+
+  float g;
+  if (renorm) {
+    const float mx = wave_max(lane < K ? my_l : -INFINITY);
+    const float ex = lane < K ? expf(my_l - mx) : 0.f;
+    g = ex / wave_sum(ex);
+  } else {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < R; ++r) mx = fmaxf(mx, lg[r]);
+    mx = wave_max(mx);
+    float z = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) z += (r * 64 + lane < E) ? expf(lg[r] - mx) : 0.f;
+    z = wave_sum(z);
+    g = expf(my_l - mx) / z;
+  }
+  if (lane < K) {
+    idx_out[t * K + lane] = my_e;
+    gate_out[t * K + lane] = g;
+  }
+}
+
+// Scores x . W_r (+ router_bias) on the vector ALUs, then selection.  EC
+// experts are accumulated per pass over the token row.
+template <typename T, int EC, int R>
+__global__ void __launch_bounds__(64 * ROUTER_WAVES)
+router_fused_kernel(int64_t S, int d, int E, int K, const T* __restrict__ x,
+                    const T* __restrict__ Wr, const float* __restrict__ rbias,
+                    const float* __restrict__ sbias, int n_groups, int topk_groups, int renorm,
+                    float* __restrict__ logits_out, int32_t* __restrict__ idx,
+                    float* __restrict__ gate) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * ROUTER_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= S) return;
+  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
+  const T* xr = x + t * d;
+  float lg[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) lg[r] = -INFINITY;
+
+  for (int e0 = 0; e0 < E; e0 += EC) {
+    float acc[EC];
+#pragma unroll
+    for (int j = 0; j < EC; ++j) acc[j] = 0.f;
+    for (int i0 = lane * VEC; i0 < d; i0 += 64 * VEC) {
+      float xv[VEC];
+      if constexpr (sizeof(T) == 2) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(xr + i0);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { xv[2 * q] = bf16_bits_to_f32(w[q] & 0xffff); xv[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16); }
+      } else {
+        const float4 raw = *reinterpret_cast<const float4*>(xr + i0);
+        xv[0] = raw.x; xv[1] = raw.y; xv[2] = raw.z; xv[3] = raw.w;
+      }
+#pragma unroll
+      for (int j = 0; j < EC; ++j) {
+        if (e0 + j < E) {
+          const T* wr = Wr + (int64_t)(e0 + j) * d + i0;
+          float s = acc[j];
+          if constexpr (sizeof(T) == 2) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(wr);
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              s = fmaf(xv[2 * q], bf16_bits_to_f32(w[q] & 0xffff), s);
+              s = fmaf(xv[2 * q + 1], bf16_bits_to_f32(w[q] >> 16), s);
+            }
+          } else {
+            const float4 raw = *reinterpret_cast<const float4*>(wr);
+            s = fmaf(xv[0], raw.x, s); s = fmaf(xv[1], raw.y, s);
+            s = fmaf(xv[2], raw.z, s); s = fmaf(xv[3], raw.w, s);
+          }
+          acc[j] = s;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < EC; ++j) {
+      const float tot = wave_sum(acc[j]);
+      const int e = e0 + j;
+      if (e < E) {
+        const float l = rbias != nullptr ? tot + rbias[e] : tot;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (r * 64 + lane == e) lg[r] = l;
+      }
+    }
+  }
+  if (logits_out != nullptr) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r * 64 + lane < E) logits_out[t * E + r * 64 + lane] = lg[r];
+  }
+  select_and_gate<R>(lg, E, K, sbias, n_groups, topk_groups, renorm, t, idx, gate);
+}
+
+// Selection from precomputed float32 scores [S][E].
+template <int R>
+__global__ void __launch_bounds__(64 * ROUTER_WAVES)
+route_logits_kernel(int64_t S, int E, int K, const float* __restrict__ logits,
+                    const float* __restrict__ sbias, int n_groups, int topk_groups, int renorm,
+                    float* __restrict__ logits_copy, int32_t* __restrict__ idx,
+                    float* __restrict__ gate) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * ROUTER_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= S) return;
+  float lg[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = r * 64 + lane;
+    lg[r] = e < E ? logits[t * E + e] : -INFINITY;
+    if (logits_copy != nullptr && e < E) logits_copy[t * E + e] = lg[r];
+  }
+  select_and_gate<R>(lg, E, K, sbias, n_groups, topk_groups, renorm, t, idx, gate);
+}
+
+// ------------------------------------------------------------------ launchers
+template <typename T, int EC>
+static hipError_t launch_fused_T(const Problem& p, const void* x, const void* Wr, const float* rb,
+                                 const float* sb, float* lo, int32_t* idx, float* gate,
+                                 hipStream_t st) {
+  const int R = (p.E + 63) / 64;
+  const dim3 grid((unsigned)ceil_div(p.S, ROUTER_WAVES)), block(64 * ROUTER_WAVES);
+#define SFL_FUSED(RR)                                                                           \
+  router_fused_kernel<T, EC, RR><<<grid, block, 0, st>>>(p.S, p.d, p.E, p.K, (const T*)x,      \
+                                                         (const T*)Wr, rb, sb, p.n_groups,      \
+                                                         p.topk_groups, p.renormalize, lo, idx, \
+                                                         gate)
+  switch (R) {
+    case 1: SFL_FUSED(1); break;
+    case 2: SFL_FUSED(2); break;
+    case 3: case 4: SFL_FUSED(4); break;
+    default: SFL_FUSED(8); break;
+  }
+#undef SFL_FUSED
+  return hipGetLastError();
+}
+
+hipError_t launch_router_fused(const Problem& p, const void* x, const void* Wr, const float* rb,
+                               const float* sb, float* logits_out, int32_t* idx, float* gate,
+                               hipStream_t st) {
+  if (p.act == DT_BF16) {
+    if (p.E <= 8) return launch_fused_T<uint16_t, 8>(p, x, Wr, rb, sb, logits_out, idx, gate, st);
+    return launch_fused_T<uint16_t, 32>(p, x, Wr, rb, sb, logits_out, idx, gate, st);
+  }
+  if (p.E <= 8) return launch_fused_T<float, 8>(p, x, Wr, rb, sb, logits_out, idx, gate, st);
+  return launch_fused_T<float, 32>(p, x, Wr, rb, sb, logits_out, idx, gate, st);
+}
+
+hipError_t launch_route_logits(const Problem& p, const float* logits, const float* sb,
+                               float* logits_copy, int32_t* idx, float* gate, hipStream_t st) {
+  const int R = (p.E + 63) / 64;
+  const dim3 grid((unsigned)ceil_div(p.S, ROUTER_WAVES)), block(64 * ROUTER_WAVES);
+#define SFL_ROUTE(RR)                                                                         \
+  route_logits_kernel<RR><<<grid, block, 0, st>>>(p.S, p.E, p.K, logits, sb, p.n_groups,     \
+                                                  p.topk_groups, p.renormalize, logits_copy, \
+                                                  idx, gate)
+  switch (R) {
+    case 1: SFL_ROUTE(1); break;
+    case 2: SFL_ROUTE(2); break;
+    case 3: case 4: SFL_ROUTE(4); break;
+    default: SFL_ROUTE(8); break;
+  }
+#undef SFL_ROUTE
+  return hipGetLastError();
+}
+
+}  // namespace sfl

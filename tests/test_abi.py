@@ -1,0 +1,157 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol declared in
+include/moe.h, matches the header's struct layout, and rejects invalid
+arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import sparse_ffn_layer_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    lib = M.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", M.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header():
+    code = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "moe.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_problem),
+    offsetof(moe_problem, S), offsetof(moe_problem, d), offsetof(moe_problem, d_ff),
+    offsetof(moe_problem, E), offsetof(moe_problem, K), offsetof(moe_problem, n_groups),
+    offsetof(moe_problem, topk_groups), offsetof(moe_problem, renormalize),
+    offsetof(moe_problem, act_dtype), offsetof(moe_problem, w_dtype));
+  return 0;
+}'''
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(c, "w").write(code)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        vals = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    P = M.moe_problem
+    mine = [ctypes.sizeof(P)] + [getattr(P, f).offset for f, _ in P._fields_]
+    assert vals == mine
+
+
+def prob(**kw):
+    base = dict(S=64, d=128, d_ff=256, E=8, K=2, act="bf16", w="bf16")
+    base.update(kw)
+    return M.make_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=9), M.MOE_ERR_INVALID_ARG),
+    (dict(K=0), M.MOE_ERR_INVALID_ARG),
+    (dict(E=0), M.MOE_ERR_INVALID_ARG),
+    (dict(S=-1), M.MOE_ERR_INVALID_ARG),
+    (dict(renormalize=2), M.MOE_ERR_INVALID_ARG),
+    (dict(E=12, n_groups=4, topk_groups=2), M.MOE_ERR_INVALID_ARG),   # group of 3: not a power of 2
+    (dict(E=16, n_groups=3, topk_groups=1), M.MOE_ERR_INVALID_ARG),   # 16 % 3
+    (dict(E=16, n_groups=4, topk_groups=0), M.MOE_ERR_INVALID_ARG),
+    (dict(E=16, n_groups=4, topk_groups=5), M.MOE_ERR_INVALID_ARG),
+    (dict(E=16, n_groups=4, topk_groups=1, K=5), M.MOE_ERR_INVALID_ARG),  # K > 1 group of 4
+    (dict(act="f32", w="bf16"), M.MOE_ERR_UNSUPPORTED),
+    (dict(act="bf16", w="f32"), M.MOE_ERR_UNSUPPORTED),
+    (dict(act="f32", w="fp8"), M.MOE_ERR_UNSUPPORTED),
+    (dict(d=100), M.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=96), M.MOE_ERR_UNSUPPORTED),
+    (dict(E=1024, K=2), M.MOE_ERR_UNSUPPORTED),
+    (dict(E=128, K=65), M.MOE_ERR_UNSUPPORTED),
+    (dict(E=256, n_groups=128, topk_groups=2), M.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_problems_rejected(kw, status):
+    p = prob(**kw)
+    lib = M.lib()
+    assert lib.moe_tile_m(ctypes.byref(p)) == -1
+    assert lib.moe_rows_capacity(ctypes.byref(p)) == -1
+    assert lib.moe_workspace_bytes(ctypes.byref(p), M.STAGE_LAYER) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    args15 = [fake] * 15
+    assert lib.moe_layer_forward(ctypes.byref(p), *args15, fake, 1 << 40, None) == status
+    assert lib.moe_route(ctypes.byref(p), *([fake] * 8), fake, 1 << 40, None) == status
+    assert lib.moe_permute(ctypes.byref(p), *([fake] * 7), fake, 1 << 40, None) == status
+    assert lib.moe_expert_ffn(ctypes.byref(p), *([fake] * 11), fake, 1 << 40, None) == status
+    assert lib.moe_combine(ctypes.byref(p), *([fake] * 4), None) == status
+
+
+def test_null_problem_and_status_strings():
+    lib = M.lib()
+    assert lib.moe_tile_m(None) == -1
+    assert lib.moe_route(None, *([None] * 8), None, 0, None) == M.MOE_ERR_INVALID_ARG
+    for s, txt in ((0, "ok"), (-1, "invalid"), (-2, "unsupported"), (-3, "workspace"), (-4, "HIP")):
+        assert txt in M.moe_status_string(s)
+
+
+def test_pointer_and_workspace_checks_precede_launch():
+    lib = M.lib()
+    p = prob()
+    a = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced
+    odd = ctypes.c_void_p((1 << 20) + 4)  # misaligned
+    ws_need = M.moe_workspace_bytes(p, M.STAGE_LAYER)
+    assert ws_need > 0
+    base = [a, a, None, None, a, a, a, a, None, None, a, None, None, None, None]
+    # missing required pointer
+    bad = list(base); bad[0] = None
+    assert lib.moe_layer_forward(ctypes.byref(p), *bad, a, ws_need, None) == M.MOE_ERR_INVALID_ARG
+    # misaligned pointer
+    bad = list(base); bad[4] = odd
+    assert lib.moe_layer_forward(ctypes.byref(p), *bad, a, ws_need, None) == M.MOE_ERR_INVALID_ARG
+    # workspace too small / missing
+    assert lib.moe_layer_forward(ctypes.byref(p), *base, a, ws_need - 1, None) == M.MOE_ERR_WORKSPACE
+    assert lib.moe_layer_forward(ctypes.byref(p), *base, None, ws_need, None) == M.MOE_ERR_WORKSPACE
+    # fp8 weights without scales
+    p8 = prob(w="fp8")
+    assert lib.moe_layer_forward(ctypes.byref(p8), *base, a, 1 << 40, None) == M.MOE_ERR_INVALID_ARG
+    # route: logits_in lets x / W_r be NULL, but outputs are required
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, a, None, None, a, None, 0, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, None, None, a, a, None, 0, None) == M.MOE_ERR_INVALID_ARG
+    pw = prob(E=64, K=4)   # router product on the MFMA path needs a logits workspace
+    assert M.moe_workspace_bytes(pw, M.STAGE_ROUTE) == 64 * 64 * 4
+    assert lib.moe_route(ctypes.byref(pw), a, a, None, None, None, None, a, a, None, 0, None) == M.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(ctypes.byref(p), a, a, a, a, a, a, a, None, 0, None) == M.MOE_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_noop_without_device():
+    lib = M.lib()
+    p = prob(S=0)
+    assert lib.moe_layer_forward(ctypes.byref(p), *([None] * 15), None, 0, None) == M.MOE_OK
+    assert lib.moe_route(ctypes.byref(p), *([None] * 8), None, 0, None) == M.MOE_OK
+    assert lib.moe_permute(ctypes.byref(p), *([None] * 7), None, 0, None) == M.MOE_OK
+    assert lib.moe_expert_ffn(ctypes.byref(p), *([None] * 11), None, 0, None) == M.MOE_OK
+    assert lib.moe_combine(ctypes.byref(p), *([None] * 4), None) == M.MOE_OK
+
+
+@pytest.mark.parametrize("S,E,K", [(4096, 8, 2), (16, 8, 2), (8192, 64, 4), (4096, 256, 8), (1, 8, 2), (3, 512, 64)])
+def test_capacity_formula(S, E, K):
+    p = prob(S=S, E=E, K=K, d=4096, d_ff=14336)
+    tm = M.moe_tile_m(p)
+    assert tm in (16, 64, 128)
+    pairs = S * K
+    assert M.moe_rows_capacity(p) == pairs + min(E, pairs) * (tm - 1)
+    cap = M.moe_rows_capacity(p)
+    ws = M.moe_workspace_bytes(p, M.STAGE_LAYER)
+    assert ws >= cap * (2 * 4096 + 14336) * 2

@@ -1,0 +1,341 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI (MI355X).
+
+Stage tests feed each entry point the oracle's own intermediate results
+(logits, indices, permutation, expert outputs) so that integer results must
+match bit for bit and floating-point results within the stated tolerance.
+Layer tests run the whole forward on all five workloads; at full size the
+oracle computes a sample of tokens one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen as D
+import oracle as O
+import sparse_ffn_layer_amd as M
+from tests._util import raw
+from tests.gpu_common import (DEV, GATE_TOL, act_from_raw, gpu_inputs, near_tie, oracle_logits,
+                              oracle_select, oracle_view, problem, sample_tokens, tol_of)
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["tiny_f32", "mixtral_prefill", "decode", "zipf_skew", "dsv3_fp8"]
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ input generation
+def test_datagen_gpu_bits_equal_cpu():
+    """The generator is device-independent: GPU tensors equal CPU ones bit for bit."""
+    for name in ("tiny_f32", "dsv3_fp8"):
+        cfg = D.CONFIGS[name]
+        if name == "tiny_f32":
+            a, b = D.make_inputs(cfg, "cpu"), D.make_inputs(cfg, DEV)
+            keys = [k for k in a if a[k] is not None]
+            for k in keys:
+                assert np.array_equal(raw(a[k]), raw(b[k])), k
+        else:
+            for e in (0, 137):
+                a, b = D.expert_weights(cfg, e, "cpu"), D.expert_weights(cfg, e, DEV)
+                for k in a:
+                    assert np.array_equal(raw(a[k]), raw(b[k])), (e, k)
+            assert np.array_equal(raw(D.tokens(cfg, "cpu", 100, 7)), raw(D.tokens(cfg, DEV, 100, 7)))
+
+
+# ------------------------------------------------------------------ route
+def _route_case(cfg, logits, sbias=None):
+    p = problem(cfg, S=logits.shape[0])
+    lg = torch.from_numpy(logits).to(DEV)
+    sb = None if sbias is None else torch.from_numpy(sbias).to(DEV)
+    idx, gate = M.moe_route(p, None, None, select_bias=sb, logits_in=lg)
+    sync()
+    o_idx = O.select_experts(logits, cfg.K, sbias, cfg.n_groups, cfg.topk_groups)
+    o_gate = O.gate_weights(logits, o_idx, cfg.renormalize)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    np.testing.assert_allclose(gate.cpu().numpy(), o_gate, rtol=0, atol=GATE_TOL)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_route_given_oracle_logits(name):
+    cfg = D.CONFIGS[name]
+    inp = gpu_inputs(name)
+    ov = oracle_view(inp)
+    logits = oracle_logits(cfg, ov)
+    _route_case(cfg, logits, ov["select_bias"])
+    _route_case(cfg.replace(renormalize=0), logits, ov["select_bias"])
+
+
+@pytest.mark.parametrize("E,K,G,tg", [(8, 2, 1, 1), (8, 8, 1, 1), (64, 4, 1, 1), (64, 6, 8, 2),
+                                      (256, 8, 8, 2), (256, 8, 2, 1), (512, 64, 4, 2), (5, 3, 1, 1),
+                                      (100, 7, 1, 1), (512, 16, 64, 3)])
+def test_route_ties_and_groups(E, K, G, tg):
+    """Small-integer scores force ties in keys and group sums; lower index wins."""
+    rng = np.random.default_rng(E * 7 + K)
+    S = 300
+    logits = rng.integers(-3, 4, size=(S, E)).astype(np.float32)
+    sb = rng.integers(-1, 2, size=E).astype(np.float32) if G > 1 else None
+    cfg = D.MoEConfig("t", S=S, d=64, d_ff=64, E=E, K=K, n_groups=G, topk_groups=tg)
+    _route_case(cfg, logits, sb)
+    _route_case(cfg, (logits + rng.standard_normal((S, E)).astype(np.float32)).astype(np.float32), sb)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_router_logits_within_error_bound(name):
+    """GPU scores (x W_r^T + bias in fp32) vs the oracle's exact-then-rounded
+    scores: |dl| <= (d + 2) 2^-24 sum_i |x_i w_i| + 2^-23 |l|."""
+    cfg = D.CONFIGS[name]
+    inp = gpu_inputs(name)
+    p = problem(cfg)
+    lo = torch.empty((cfg.S, cfg.E), dtype=torch.float32, device=DEV)
+    idx, gate = M.moe_route(p, inp["x"], inp["W_r"], inp["router_bias"], inp["select_bias"], logits_out=lo)
+    sync()
+    ov = oracle_view(inp)
+    ref = oracle_logits(cfg, ov).astype(np.float64)
+    bound = logit_bound(cfg, ov, ref) + 1e-30
+    got = lo.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bound)
+    # routing from the GPU's own scores differs from the oracle's only at near-ties
+    o_idx, _ = oracle_select(cfg, ref.astype(np.float32), ov)
+    g_idx = idx.cpu().numpy()
+    for t in np.nonzero(np.any(g_idx != o_idx, axis=1))[0]:
+        assert routing_mismatch_is_near_tie(cfg, ov, ref.astype(np.float32), bound, t), t
+
+
+# ------------------------------------------------------------------ permute
+def _permute_case(E, K, idx, d=64, act="bf16"):
+    S = idx.shape[0]
+    cfg = D.MoEConfig("p", S=S, d=d, d_ff=64, E=E, K=K, act=act, w="f32" if act == "f32" else "bf16")
+    p = problem(cfg)
+    tm = M.moe_tile_m(p)
+    x = D.tokens(cfg, DEV)
+    counts, offsets, perm, inv, x_perm = M.moe_permute(p, torch.from_numpy(idx).to(DEV), x)
+    sync()
+    ref = O.permute(idx, E, tm)
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+    assert np.array_equal(inv.cpu().numpy(), ref["inv_perm"])
+    rows = torch.from_numpy(ref["inv_perm"].astype(np.int64)).to(DEV)
+    tok = torch.arange(S * K, device=DEV) // K
+    assert torch.equal(x_perm[rows].view(torch.int16 if act == "bf16" else torch.int32),
+                       x[tok].view(torch.int16 if act == "bf16" else torch.int32))
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_permute_given_oracle_indices(name):
+    cfg = D.CONFIGS[name]
+    inp = gpu_inputs(name)
+    ov = oracle_view(inp)
+    idx, _ = oracle_select(cfg, oracle_logits(cfg, ov), ov)
+    p = problem(cfg)
+    counts, offsets, perm, inv, x_perm = M.moe_permute(p, torch.from_numpy(idx).to(DEV), inp["x"])
+    sync()
+    ref = O.permute(idx, cfg.E, M.moe_tile_m(p))
+    for got, key in ((counts, "counts"), (offsets, "offsets"), (perm, "perm"), (inv, "inv_perm")):
+        assert np.array_equal(got.cpu().numpy(), ref[key]), key
+    rows = torch.from_numpy(ref["inv_perm"].astype(np.int64)).to(DEV)
+    tok = torch.arange(cfg.S * cfg.K, device=DEV) // cfg.K
+    assert torch.equal(x_perm[rows], inp["x"][tok])
+    if name == "zipf_skew":
+        assert (ref["counts"] == 0).sum() > 0     # empty experts exercised
+
+
+@pytest.mark.parametrize("S,E,K", [(1, 8, 2), (2, 512, 64), (5000, 64, 4), (3001, 256, 8), (70000, 8, 2), (17, 3, 3)])
+def test_permute_shapes(S, E, K):
+    rng = np.random.default_rng(S + E)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(S)]).astype(np.int32)
+    _permute_case(E, K, idx)
+
+
+def test_permute_all_tokens_one_expert_set():
+    S, E, K = 4099, 64, 4
+    idx = np.tile(np.arange(K, dtype=np.int32)[::-1], (S, 1)).copy()
+    _permute_case(E, K, idx, act="f32")
+
+
+# ------------------------------------------------------------------ expert FFN
+def _expert_case(cfg, inp, ov, pairs_sel=None):
+    """Oracle permutation -> x_perm built on the host -> GPU FFN; compare the
+    h and y_perm rows of the selected pairs with the oracle's expert FFN."""
+    p = problem(cfg)
+    tm = M.moe_tile_m(p)
+    idx, _ = oracle_select(cfg, oracle_logits(cfg, ov), ov)
+    pm = O.permute(idx, cfg.E, tm)
+    cap = M.moe_rows_capacity(p)
+    xr = ov["x"]
+    xp = np.zeros((cap, cfg.d), dtype=xr.dtype)
+    flat_t = np.arange(cfg.S * cfg.K) // cfg.K
+    xp[pm["inv_perm"]] = xr[flat_t]
+    x_perm = act_from_raw(xp, cfg.act)
+    counts = torch.from_numpy(pm["counts"]).to(DEV)
+    offsets = torch.from_numpy(pm["offsets"]).to(DEV)
+    h, y_perm = M.moe_expert_ffn(p, x_perm, counts, offsets, inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                                 inp["w1_scale"], inp["w2_scale"])
+    sync()
+    pairs = np.arange(cfg.S * cfg.K) if pairs_sel is None else pairs_sel
+    flat_e = idx.reshape(-1)
+    hmax = ymax = 0.0
+    herr = yerr = 0.0
+    for e in np.unique(flat_e[pairs]):
+        ps = pairs[flat_e[pairs] == e]
+        x64 = O.decode(xr[flat_t[ps]], cfg.act)
+        W1e = O.expert_matrix(ov["W1"][e], cfg.w, None if ov["w1_scale"] is None else ov["w1_scale"][e])
+        W2e = O.expert_matrix(ov["W2"][e], cfg.w, None if ov["w2_scale"] is None else ov["w2_scale"][e])
+        hr, yr = O.expert_ffn(x64, W1e, O.decode(ov["b1"][e], cfg.act), W2e, O.decode(ov["b2"][e], cfg.act),
+                              return_hidden=True)
+        rows = pm["inv_perm"][ps]
+        hg = O.decode(raw(h[torch.from_numpy(rows.astype(np.int64)).to(DEV)]), cfg.act)
+        yg = O.decode(raw(y_perm[torch.from_numpy(rows.astype(np.int64)).to(DEV)]), cfg.act)
+        herr, hmax = max(herr, np.abs(hg - hr).max()), max(hmax, np.abs(hr).max())
+        yerr, ymax = max(yerr, np.abs(yg - yr).max()), max(ymax, np.abs(yr).max())
+    t = tol_of(cfg)
+    assert herr <= t * hmax, (herr, hmax)
+    assert yerr <= t * ymax, (yerr, ymax)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_expert_ffn_given_oracle_permutation(name):
+    cfg = D.CONFIGS[name]
+    inp = gpu_inputs(name)
+    ov = oracle_view(inp)
+    sel = None
+    if cfg.S * cfg.K > 1024:   # full size: a sample of pairs, including the last one
+        sel = sample_tokens(cfg.S * cfg.K, 48 if cfg.E <= 64 else 16, seed=1)
+    _expert_case(cfg, inp, ov, sel)
+
+
+# ------------------------------------------------------------------ combine
+@pytest.mark.parametrize("act,S,d,K,E", [("bf16", 333, 256, 2, 8), ("f32", 64, 128, 2, 8), ("bf16", 50, 7168, 8, 256)])
+def test_combine_given_oracle_inputs(act, S, d, K, E):
+    cfg = D.MoEConfig("c", S=S, d=d, d_ff=64, E=E, K=K, act=act, w="f32" if act == "f32" else "bf16")
+    p = problem(cfg)
+    rng = np.random.default_rng(S)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(S)]).astype(np.int32)
+    pm = O.permute(idx, E, M.moe_tile_m(p))
+    cap = M.moe_rows_capacity(p)
+    yp = D.store(D.normal(0, ("yperm",), (cap, d), 1.0), act)
+    gates = rng.random((S, K)).astype(np.float32)
+    y = M.moe_combine(p, yp.to(DEV), torch.from_numpy(pm["inv_perm"]).to(DEV), torch.from_numpy(gates).to(DEV))
+    sync()
+    outs = O.decode(raw(yp), act)[pm["inv_perm"].reshape(S, K)]
+    ref = O.combine(gates.astype(np.float64), outs)
+    got = O.decode(raw(y), act)
+    t = 2.0 ** -8 if act == "bf16" else 2.0 ** -22
+    assert np.all(np.abs(got - ref) <= t * np.abs(ref) + 1e-6 * np.abs(outs).max())
+
+
+# ------------------------------------------------------------------ whole layer
+def logit_bound(cfg, ov, ref):
+    """Rounding bound of fp32 router scores against the exact product."""
+    x, w = O.decode(ov["x"], cfg.act), O.decode(ov["W_r"], cfg.act)
+    return (cfg.d + 2) * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T) + 2.0 ** -23 * np.abs(ref)
+
+
+def routing_mismatch_is_near_tie(cfg, ov, ref_logits, bound, t):
+    """A token may route differently on the GPU only if its oracle keys (or,
+    with a group limit, its group scores) tie within the score error."""
+    keys = ref_logits[t].astype(np.float64)
+    if ov["select_bias"] is not None:
+        keys = keys + ov["select_bias"]
+    gap = 4 * bound[t].max()
+    if cfg.n_groups > 1:
+        m = cfg.E // cfg.n_groups
+        gs = keys.reshape(cfg.n_groups, m).sum(1)
+        if near_tie(gs, cfg.topk_groups, gap * m):
+            return True
+    return near_tie(keys, cfg.K, gap)
+
+
+def _layer_case(cfg, inp, tokens):
+    p = problem(cfg)
+    idx_out = torch.empty((cfg.S, cfg.K), dtype=torch.int32, device=DEV)
+    gate_out = torch.empty((cfg.S, cfg.K), dtype=torch.float32, device=DEV)
+    counts_out = torch.empty((cfg.E,), dtype=torch.int32, device=DEV)
+    y = M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                            inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"],
+                            topk_idx_out=idx_out, topk_gate_out=gate_out, expert_counts_out=counts_out)
+    sync()
+    ov = oracle_view(inp)
+    g_idx = idx_out.cpu().numpy()
+    assert np.array_equal(counts_out.cpu().numpy(), np.bincount(g_idx.reshape(-1), minlength=cfg.E))
+    # the oracle routes every token from its own scores
+    ref_logits = oracle_logits(cfg, ov)
+    o_idx, o_gate = oracle_select(cfg, ref_logits, ov)
+    same_all = np.all(o_idx == g_idx, axis=1)
+    if not same_all.all():
+        bound = logit_bound(cfg, ov, ref_logits.astype(np.float64))
+        for t in np.nonzero(~same_all)[0]:
+            assert routing_mismatch_is_near_tie(cfg, ov, ref_logits, bound, t), t
+    np.testing.assert_allclose(gate_out.cpu().numpy()[same_all], o_gate[same_all], atol=1e-5, rtol=0)
+    # the oracle's whole forward on the sampled tokens
+    ref = O.layer_forward(ov["x"], ov["W_r"], ov["W1"], ov["b1"], ov["W2"], ov["b2"], K=cfg.K,
+                          act=cfg.act, w=cfg.w, router_bias=ov["router_bias"],
+                          select_bias=ov["select_bias"], n_groups=cfg.n_groups,
+                          topk_groups=cfg.topk_groups, renormalize=cfg.renormalize,
+                          w1_scale=ov["w1_scale"], w2_scale=ov["w2_scale"], tokens=tokens,
+                          return_parts=True)
+    same = same_all[tokens]
+    assert same.mean() >= 0.9
+    yg = O.decode(raw(y[torch.from_numpy(np.asarray(tokens)).to(DEV)]), cfg.act)
+    yr = ref["y"]
+    t = tol_of(cfg)
+    err = np.abs(yg[same] - yr[same]).max()
+    assert err <= t * np.abs(yr).max(), (err, np.abs(yr).max())
+    return y
+
+
+SAMPLE = {"tiny_f32": 64, "mixtral_prefill": 48, "decode": 16, "zipf_skew": 48, "dsv3_fp8": 8}
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_layer_forward(name):
+    cfg = D.CONFIGS[name]
+    inp = gpu_inputs(name)
+    _layer_case(cfg, inp, sample_tokens(cfg.S, SAMPLE[name], seed=2))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(S=1, d=128, d_ff=256, E=8, K=2),                          # single token
+    dict(S=37, d=192, d_ff=320, E=1, K=1),                         # E=1: dense FFN
+    dict(S=29, d=128, d_ff=128, E=8, K=8),                         # K=E: soft routing
+    dict(S=301, d=256, d_ff=192, E=64, K=6, n_groups=8, topk_groups=2),  # group-limited, MFMA router
+    dict(S=77, d=128, d_ff=256, E=16, K=2, renormalize=0),         # raw softmax gates
+    dict(S=5, d=256, d_ff=512, E=256, K=8, n_groups=8, topk_groups=2, w="fp8"),  # fp8, decode regime
+    dict(S=1500, d=256, d_ff=384, E=8, K=2),                       # prefill regime, ragged tiles
+    dict(S=333, d=128, d_ff=256, E=32, K=3, act="f32", w="f32"),   # fp32 path
+    dict(S=64, d=512, d_ff=256, E=128, K=4, w="fp8"),              # mid regime fp8
+])
+def test_layer_edge_cases(kw):
+    cfg = D.MoEConfig("edge", **kw)
+    if cfg.select_bias_var == 0 and cfg.n_groups > 1:
+        cfg = cfg.replace(select_bias_var=0.1)
+    inp = D.make_inputs(cfg, DEV)
+    _layer_case(cfg, inp, np.arange(cfg.S))
+
+
+def test_empty_batch_noop():
+    cfg = D.CONFIGS["tiny_f32"]
+    p = problem(cfg, S=0)
+    inp = gpu_inputs("tiny_f32")
+    y = torch.full((1, cfg.d), 7.0, device=DEV)
+    M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"], y=y)
+    sync()
+    assert torch.all(y == 7.0)
+
+
+@pytest.mark.parametrize("name", ["zipf_skew", "decode"])
+def test_deterministic(name):
+    cfg = D.CONFIGS[name]
+    inp = gpu_inputs(name)
+    p = problem(cfg)
+    outs = []
+    for _ in range(2):
+        c = torch.empty(cfg.E, dtype=torch.int32, device=DEV)
+        y = M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                                inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"],
+                                expert_counts_out=c)
+        sync()
+        outs.append((raw(y).copy(), c.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
