@@ -1,0 +1,261 @@
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+One step = one moe_layer_forward (route, permute, expert up/down GEMMs,
+combine) over the workload's S tokens, inputs resident in HBM.  Prints ONE
+JSON line on stdout: MoE-layer tokens/s at the Mixtral-shape prefill workload
+(S=4096, d=4096, d_ff=14336, E=8, K=2, bf16), the roofline of the dominant
+kernel, the decode workload's HBM fraction, and the CPU oracle's rate on a
+bounded sample of the same workload.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--no-decode]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA, MI355X
+PEAK_GBS = 8000.0                                             # HBM3E
+METRIC = "MoE-layer tokens/s at Mixtral shape; % MFMA peak (prefill), % HBM BW (decode)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+class Workload:
+    """Device inputs, outputs and stage buffers of one configuration."""
+
+    def __init__(self, cfg, D, M, torch):
+        self.cfg, self.M, self.torch = cfg, M, torch
+        dev = "cuda"
+        t0 = time.time()
+        self.inp = D.make_inputs(cfg, dev)
+        torch.cuda.synchronize()
+        log(f"[bench] {cfg.name}: inputs generated in {time.time() - t0:.1f}s")
+        c = cfg
+        self.p = M.make_problem(c.S, c.d, c.d_ff, c.E, c.K, c.act, c.w, c.n_groups, c.topk_groups, c.renormalize)
+        act = torch.bfloat16 if c.act == "bf16" else torch.float32
+        cap = M.moe_rows_capacity(self.p)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.y = torch.empty((c.S, c.d), dtype=act, device=dev)
+        self.ws = M.workspace(self.p, M.STAGE_LAYER, dev)
+        self.counts = torch.empty(c.E, **i32)
+        # stage buffers
+        self.idx = torch.empty((c.S, c.K), **i32)
+        self.gate = torch.empty((c.S, c.K), dtype=torch.float32, device=dev)
+        self.ws_route = M.workspace(self.p, M.STAGE_ROUTE, dev)
+        self.ws_perm = M.workspace(self.p, M.STAGE_PERMUTE, dev)
+        self.offsets = torch.empty(c.E + 1, **i32)
+        self.perm = torch.empty(c.S * c.K, **i32)
+        self.inv = torch.empty(c.S * c.K, **i32)
+        self.x_perm = torch.empty((cap, c.d), dtype=act, device=dev)
+        self.h = torch.empty((cap, c.d_ff), dtype=act, device=dev)
+        self.y_perm = torch.empty((cap, c.d), dtype=act, device=dev)
+        self.y2 = torch.empty((c.S, c.d), dtype=act, device=dev)
+
+    def layer(self):
+        i, M = self.inp, self.M
+        M.moe_layer_forward(self.p, i["x"], i["W_r"], i["W1"], i["b1"], i["W2"], i["b2"], i["router_bias"],
+                            i["select_bias"], i["w1_scale"], i["w2_scale"], y=self.y,
+                            expert_counts_out=self.counts, ws=self.ws)
+
+    def stages(self):
+        i, M, p = self.inp, self.M, self.p
+        return {
+            "route": lambda: M.moe_route(p, i["x"], i["W_r"], i["router_bias"], i["select_bias"],
+                                         topk_idx=self.idx, topk_gate=self.gate, ws=self.ws_route),
+            "permute": lambda: M.moe_permute(p, self.idx, i["x"], self.counts, self.offsets, self.perm,
+                                             self.inv, self.x_perm, ws=self.ws_perm),
+            "expert_up": lambda: M.moe_expert_up(p, self.x_perm, self.counts, self.offsets, i["W1"], i["b1"],
+                                                 i["w1_scale"], h=self.h),
+            "expert_down": lambda: M.moe_expert_down(p, self.h, self.counts, self.offsets, i["W2"], i["b2"],
+                                                     i["w2_scale"], y_perm=self.y_perm),
+            "combine": lambda: M.moe_combine(p, self.y_perm, self.inv, self.gate, y=self.y2),
+        }
+
+
+def time_calls(torch, fn, steps, warmup):
+    """Average ms per call, HIP events on the stream the library launches on."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def algorithmic(cfg, touched):
+    """Per-launch algorithmic flops and HBM bytes of the two expert GEMMs.
+
+    Flops count only the S*K routed rows (no padding).  Bytes: each touched
+    expert's weights (+ fp8 scales) and biases once, the routed activation
+    rows in and out once."""
+    a = 2 if cfg.act == "bf16" else 4
+    w = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.w]
+    rows = cfg.S * cfg.K
+    fl = 2.0 * rows * cfg.d * cfg.d_ff
+    sc = 4 if cfg.w == "fp8" else 0
+    up = touched * (cfg.d * cfg.d_ff * w + cfg.d_ff * (a + sc)) + rows * (cfg.d + cfg.d_ff) * a
+    down = touched * (cfg.d_ff * cfg.d * w + cfg.d * (a + sc)) + rows * (cfg.d_ff + cfg.d) * a
+    return {"expert_up": (fl, up), "expert_down": (fl, down)}
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "sparse_ffn_layer_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def roofline(cfg, stage_ms, touched, workload):
+    alg = algorithmic(cfg, touched)
+    name = max(("expert_up", "expert_down"), key=lambda k: stage_ms[k])
+    fl, by = alg[name]
+    sec = stage_ms[name] / 1e3
+    intensity = fl / by
+    peak_f = PEAK_TFLOPS["bf16" if cfg.act == "bf16" else "f32"]
+    ridge = peak_f * 1e12 / (PEAK_GBS * 1e9)
+    if intensity >= ridge:
+        ach, peak, unit, bound = fl / sec / 1e12, peak_f, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = by / sec / 1e9, PEAK_GBS, "GB/s", "hbm"
+    return {"kernel": name, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": traffic_for(name, workload),
+            "avg_launch_ms": round(stage_ms[name], 4), "algorithmic_flops": fl, "algorithmic_bytes": by}
+
+
+def run_workload(name, steps, warmup, D, M, torch):
+    cfg = D.CONFIGS[name]
+    w = Workload(cfg, D, M, torch)
+    ms = time_calls(torch, w.layer, steps, warmup)
+    counts = w.counts.cpu()
+    touched = int((counts > 0).sum())
+    stage_ms = {k: time_calls(torch, fn, steps, max(2, warmup // 2)) for k, fn in w.stages().items()}
+    return cfg, w, ms, stage_ms, touched, counts
+
+
+def cpu_baseline(cfg, w, target_s, torch):
+    """The oracle, as it is, on the first n tokens of the same workload."""
+    import numpy as np
+
+    import oracle as O
+    from threadpoolctl import threadpool_info
+
+    def raw(t):
+        t = t.detach().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).numpy()
+        return t.numpy()
+
+    inp = w.inp
+    host = {k: (None if v is None else raw(v)) for k, v in inp.items() if k not in ("W1", "W2")}
+    W1 = {}
+    W2 = {}
+
+    def run(n):
+        x = host["x"][:n]
+        lg = O.router_logits(O.decode(x, cfg.act), O.decode(host["W_r"], cfg.act), host["router_bias"])
+        used = np.unique(O.select_experts(lg, cfg.K, host["select_bias"], cfg.n_groups, cfg.topk_groups))
+        for e in used:   # device -> host copies stay outside the timed region
+            if int(e) not in W1:
+                W1[int(e)], W2[int(e)] = raw(inp["W1"][int(e)]), raw(inp["W2"][int(e)])
+        t0 = time.perf_counter()
+        O.layer_forward(x, host["W_r"], W1, host["b1"], W2, host["b2"], K=cfg.K, act=cfg.act, w=cfg.w,
+                        router_bias=host["router_bias"], select_bias=host["select_bias"],
+                        n_groups=cfg.n_groups, topk_groups=cfg.topk_groups, renormalize=cfg.renormalize,
+                        w1_scale=host["w1_scale"], w2_scale=host["w2_scale"])
+        return time.perf_counter() - t0
+
+    # grow the sample until it costs about target_s of CPU time (or covers S)
+    n = min(cfg.S, 32)
+    t = run(n)
+    while t < 0.5 * target_s and n < cfg.S:
+        n = int(min(cfg.S, n * min(8.0, max(2.0, target_s / max(t, 1e-3)))))
+        t = run(n)
+    threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas") or 1
+    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.S} tokens of {cfg.name}: routing, every expert they touch "
+                      f"(float64, weights decoded per expert), combine; {t:.1f}s",
+            "seconds": round(t, 2)}
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(json.dumps({"metric": METRIC, "error": "this build runs on exactly one GPU; "
+                          f"--gpus {a.gpus} (WORLD_SIZE {world}) is not supported"}))
+        sys.exit(2)
+    import torch
+
+    import datagen as D
+    import sparse_ffn_layer_amd as M
+
+    M.lib()   # raises if the HIP library is missing: there is no fallback
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    cfg, w, ms, stage_ms, touched, counts = run_workload(a.workload, a.steps, a.warmup, D, M, torch)
+    mean = cfg.S * cfg.K / cfg.E
+    out = {
+        "metric": METRIC, "value": round(cfg.S / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.act, "data": "synthetic",
+        "config": {"workload": cfg.name, "S": cfg.S, "d": cfg.d, "d_ff": cfg.d_ff, "E": cfg.E, "K": cfg.K,
+                   "weights": cfg.w, "max_over_mean_load": round(float(counts.max()) / mean, 3),
+                   "experts_touched": touched},
+        "roofline": roofline(cfg, stage_ms, touched, cfg.name),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "layer_tflops": round(4.0 * cfg.S * cfg.K * cfg.d * cfg.d_ff / (ms / 1e3) / 1e12, 2),
+    }
+    log(f"[bench] {cfg.name}: {ms:.3f} ms/step, stages {out['stage_ms']}")
+    if not a.no_decode and cfg.name != "decode":
+        dcfg, dw, dms, dstage, dtouched, _ = run_workload("decode", max(a.steps, 100), a.warmup, D, M, torch)
+        out["decode"] = {"workload": "decode", "tokens_per_s": round(dcfg.S / (dms / 1e3), 1),
+                         "ms_per_step": round(dms, 4), "roofline": roofline(dcfg, dstage, dtouched, "decode"),
+                         "stage_ms": {k: round(v, 4) for k, v in dstage.items()}}
+        del dw
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, w, a.cpu_seconds, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

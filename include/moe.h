@@ -134,7 +134,9 @@ int32_t moe_route(const moe_problem* p, const void* x, const void* W_r,
 /* Dispatch: regroup the S*K (token, slot) pairs per expert (chapter 11
  * section 11.2.1).  Pair id = t*K + k.  Within an expert pairs keep token
  * order.
- *   topk_idx [S][K] int32 in [0, E) with distinct entries per token.
+ *   topk_idx [S][K] int32 in [0, E) with distinct entries per token.  An
+ *       entry outside [0, E) is skipped: that pair gets inv_perm -1, is
+ *       counted nowhere, has no row, and moe_combine leaves it out.
  *   expert_counts [E]: pairs routed to each expert.
  *   expert_offsets [E+1]: first padded row of each expert's group; every
  *       entry is a multiple of moe_tile_m(p); entry E is the rows used.
@@ -164,10 +166,22 @@ int32_t moe_expert_ffn(const moe_problem* p, const void* x_perm,
                        const float* w1_scale, const float* w2_scale,
                        void* h, void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of moe_expert_ffn, for callers that schedule them apart:
+ *   moe_expert_up:   h[r]      = GeLU(x_perm[r] W1_e + b1_e)
+ *   moe_expert_down: y_perm[r] = h[r] W2_e + b2_e
+ * Arguments as for moe_expert_ffn (w1_scale / w2_scale required for fp8). */
+int32_t moe_expert_up(const moe_problem* p, const void* x_perm, const int32_t* expert_counts,
+                      const int32_t* expert_offsets, const void* W1, const void* b1,
+                      const float* w1_scale, void* h, void* stream);
+int32_t moe_expert_down(const moe_problem* p, const void* h, const int32_t* expert_counts,
+                        const int32_t* expert_offsets, const void* W2, const void* b2,
+                        const float* w2_scale, void* y_perm, void* stream);
+
 /* Combine (chapter 11 sections 11.1.1 and 11.2.1; "MoE 混合专家推理", one
  * MoE forward): y[t] = sum over k = 0..K-1, in slot order, of
  * topk_gate[t][k] * y_perm[inv_perm[t*K+k]], accumulated in float32 and
- * rounded once to the act dtype.  No atomics. */
+ * rounded once to the act dtype; slots with inv_perm < 0 add nothing.  No
+ * atomics. */
 int32_t moe_combine(const moe_problem* p, const void* y_perm, const int32_t* inv_perm,
                     const float* topk_gate, void* y, void* stream);
 

@@ -18,7 +18,7 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "STAGE_ROUTE", "STAGE_PERMUTE", "STAGE_EXPERT_FFN",
     "STAGE_COMBINE", "STAGE_LAYER", "MoEError", "moe_problem", "make_problem", "lib", "LIB_PATH",
     "moe_workspace_bytes", "moe_tile_m", "moe_rows_capacity", "moe_status_string",
-    "workspace", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+    "workspace", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfl_moe.so")
@@ -63,6 +63,8 @@ _SIGS = {
     "moe_route": (_i32, [_P] + [_vp] * 8 + [_vp, _sz, _vp]),
     "moe_permute": (_i32, [_P] + [_vp] * 7 + [_vp, _sz, _vp]),
     "moe_expert_ffn": (_i32, [_P] + [_vp] * 11 + [_vp, _sz, _vp]),
+    "moe_expert_up": (_i32, [_P] + [_vp] * 7 + [_vp]),
+    "moe_expert_down": (_i32, [_P] + [_vp] * 7 + [_vp]),
     "moe_combine": (_i32, [_P] + [_vp] * 4 + [_vp]),
     "moe_layer_forward": (_i32, [_P] + [_vp] * 15 + [_vp, _sz, _vp]),
 }
@@ -178,6 +180,24 @@ def moe_expert_ffn(p, x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, w1_
                               _ptr(h), _ptr(y_perm), _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_expert_ffn", st)
     return h, y_perm
+
+
+def moe_expert_up(p, x_perm, expert_counts, expert_offsets, W1, b1, w1_scale=None, h=None, stream=None):
+    if h is None:
+        h = torch.empty((moe_rows_capacity(p), p.d_ff), dtype=_act(p), device=x_perm.device)
+    st = lib().moe_expert_up(ctypes.byref(p), _ptr(x_perm), _ptr(expert_counts), _ptr(expert_offsets),
+                             _ptr(W1), _ptr(b1), _ptr(w1_scale), _ptr(h), _stream(stream))
+    _check("moe_expert_up", st)
+    return h
+
+
+def moe_expert_down(p, h, expert_counts, expert_offsets, W2, b2, w2_scale=None, y_perm=None, stream=None):
+    if y_perm is None:
+        y_perm = torch.empty((moe_rows_capacity(p), p.d), dtype=_act(p), device=h.device)
+    st = lib().moe_expert_down(ctypes.byref(p), _ptr(h), _ptr(expert_counts), _ptr(expert_offsets),
+                               _ptr(W2), _ptr(b2), _ptr(w2_scale), _ptr(y_perm), _stream(stream))
+    _check("moe_expert_down", st)
+    return y_perm
 
 
 def moe_combine(p, y_perm, inv_perm, topk_gate, y=None, stream=None):

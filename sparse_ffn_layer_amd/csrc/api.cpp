@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
+
 #include "common.h"
 
 namespace sfl {
@@ -18,9 +20,11 @@ hipError_t launch_router_gemm(const Problem&, const void*, const void*, const fl
 hipError_t launch_permute(const Problem&, int, const int32_t*, const void*, int32_t*, int32_t*,
                           int32_t*, int32_t*, void*, int32_t*, hipStream_t);
 size_t permute_scratch_ints(int64_t pairs, int E);
-hipError_t launch_expert_ffn(const Problem&, int64_t, const void*, const int32_t*,
-                             const int32_t*, const void*, const void*, const void*, const void*,
-                             const float*, const float*, void*, void*, hipStream_t);
+hipError_t launch_expert_up(const Problem&, int64_t, const void*, const int32_t*, const int32_t*,
+                            const void*, const void*, const float*, void*, hipStream_t);
+hipError_t launch_expert_down(const Problem&, int64_t, const void*, const int32_t*,
+                              const int32_t*, const void*, const void*, const float*, void*,
+                              hipStream_t);
 hipError_t launch_combine(const Problem&, const void*, const int32_t*, const float*, void*,
                           hipStream_t);
 int gemm_tile_m(const Problem& p);
@@ -107,6 +111,31 @@ LayerWs layer_layout(const Problem& p, char* base) {
 }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int32_t do_expert_ffn(const Problem& p, const void* x_perm, const int32_t* counts,
+                      const int32_t* offsets, const void* W1, const void* b1, const void* W2,
+                      const void* b2, const float* s1, const float* s2, void* h, void* y_perm,
+                      hipStream_t st) {
+  const bool fp8 = p.w == DT_FP8;
+  const int64_t cap = rows_capacity(p);
+  int32_t s = hip_status(launch_expert_up(p, cap, x_perm, counts, offsets, W1, b1, fp8 ? s1 : nullptr,
+                                          h, st));
+  if (s != MOE_OK) return s;
+  return hip_status(launch_expert_down(p, cap, h, counts, offsets, W2, b2, fp8 ? s2 : nullptr,
+                                       y_perm, st));
+}
+
+// Common checks of the expert-GEMM entry points.
+int32_t check_expert(const moe_problem* mp, Problem* p, std::initializer_list<const void*> req,
+                     const float* scale) {
+  int32_t s = check_problem(mp, p);
+  if (s != MOE_OK || p->S == 0) return s;
+  for (const void* q : req)
+    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (p->w == DT_FP8 && scale == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(scale)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
 
 int32_t do_route(const Problem& p, const void* x, const void* Wr, const float* rb, const float* sb,
                  const float* logits_in, float* logits_out, int32_t* idx, float* gate,
@@ -202,18 +231,34 @@ int32_t moe_expert_ffn(const moe_problem* mp, const void* x_perm, const int32_t*
                        void* stream) {
   (void)ws; (void)ws_bytes;
   Problem p;
-  int32_t s = check_problem(mp, &p);
-  if (s != MOE_OK) return s;
-  if (p.S == 0) return MOE_OK;
-  const void* ptrs[] = {x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, h, y_perm};
-  for (const void* q : ptrs)
-    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
-  if (p.w == DT_FP8 && (w1_scale == nullptr || w2_scale == nullptr)) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(w1_scale) || !aligned16(w2_scale)) return MOE_ERR_INVALID_ARG;
-  const bool fp8 = p.w == DT_FP8;
-  return hip_status(launch_expert_ffn(p, rows_capacity(p), x_perm, expert_counts, expert_offsets,
-                                      W1, b1, W2, b2, fp8 ? w1_scale : nullptr,
-                                      fp8 ? w2_scale : nullptr, h, y_perm, (hipStream_t)stream));
+  int32_t s = check_expert(mp, &p, {x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, h, y_perm},
+                           w1_scale);
+  if (s != MOE_OK || p.S == 0) return s;
+  if (p.w == DT_FP8 && w2_scale == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w2_scale)) return MOE_ERR_INVALID_ARG;
+  return do_expert_ffn(p, x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, w1_scale, w2_scale,
+                       h, y_perm, (hipStream_t)stream);
+}
+
+int32_t moe_expert_up(const moe_problem* mp, const void* x_perm, const int32_t* expert_counts,
+                      const int32_t* expert_offsets, const void* W1, const void* b1,
+                      const float* w1_scale, void* h, void* stream) {
+  Problem p;
+  int32_t s = check_expert(mp, &p, {x_perm, expert_counts, expert_offsets, W1, b1, h}, w1_scale);
+  if (s != MOE_OK || p.S == 0) return s;
+  return hip_status(launch_expert_up(p, rows_capacity(p), x_perm, expert_counts, expert_offsets, W1,
+                                     b1, p.w == DT_FP8 ? w1_scale : nullptr, h, (hipStream_t)stream));
+}
+
+int32_t moe_expert_down(const moe_problem* mp, const void* h, const int32_t* expert_counts,
+                        const int32_t* expert_offsets, const void* W2, const void* b2,
+                        const float* w2_scale, void* y_perm, void* stream) {
+  Problem p;
+  int32_t s = check_expert(mp, &p, {h, expert_counts, expert_offsets, W2, b2, y_perm}, w2_scale);
+  if (s != MOE_OK || p.S == 0) return s;
+  return hip_status(launch_expert_down(p, rows_capacity(p), h, expert_counts, expert_offsets, W2, b2,
+                                       p.w == DT_FP8 ? w2_scale : nullptr, y_perm,
+                                       (hipStream_t)stream));
 }
 
 int32_t moe_combine(const moe_problem* mp, const void* y_perm, const int32_t* inv_perm,
@@ -259,10 +304,8 @@ int32_t moe_layer_forward(const moe_problem* mp, const void* x, const void* W_r,
   s = hip_status(launch_permute(p, gemm_tile_m(p), idx, x, counts, w.offsets, w.perm, w.inv,
                                 w.x_perm, w.pscratch, st));
   if (s != MOE_OK) return s;
-  const bool fp8 = p.w == DT_FP8;
-  s = hip_status(launch_expert_ffn(p, rows_capacity(p), w.x_perm, counts, w.offsets, W1, b1, W2, b2,
-                                   fp8 ? w1_scale : nullptr, fp8 ? w2_scale : nullptr, w.h, w.y_perm,
-                                   st));
+  s = do_expert_ffn(p, w.x_perm, counts, w.offsets, W1, b1, W2, b2, w1_scale, w2_scale, w.h,
+                    w.y_perm, st);
   if (s != MOE_OK) return s;
   return hip_status(launch_combine(p, w.y_perm, w.inv, gate, y, st));
 }

@@ -355,36 +355,43 @@ static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hi
   }
 }
 
-// h = GeLU(x_perm W1^T + b1) and y_perm = h W2^T + b2 over the expert groups.
-hipError_t launch_expert_ffn(const Problem& p, int64_t rows_cap, const void* x_perm,
-                             const int32_t* counts, const int32_t* offsets, const void* W1,
-                             const void* b1, const void* W2, const void* b2, const float* s1,
-                             const float* s2, void* h, void* y_perm, hipStream_t st) {
-  const int regime = gemm_regime(p);
-  GemmArgs g1{};
-  g1.A = x_perm; g1.lda = p.d;
-  g1.B = W1; g1.ldb = p.d; g1.b_gstride = (int64_t)p.d_ff * p.d;
-  g1.scale = s1; g1.bias = b1;
-  g1.C = h; g1.ldc = p.d_ff;
-  g1.offsets = offsets; g1.counts = counts; g1.G = p.E;
-  g1.N = p.d_ff; g1.K = p.d;
-  GemmArgs g2 = g1;
-  g2.A = h; g2.lda = p.d_ff;
-  g2.B = W2; g2.ldb = p.d_ff; g2.b_gstride = (int64_t)p.d * p.d_ff;
-  g2.scale = s2; g2.bias = b2;
-  g2.C = y_perm; g2.ldc = p.d;
-  g2.N = p.d; g2.K = p.d_ff;
-  hipError_t err;
-  if (p.act == DT_F32) {
-    if ((err = run_f32<EPI_GELU>(g1, rows_cap, st)) != hipSuccess) return err;
-    return run_f32<EPI_BIAS>(g2, rows_cap, st);
-  }
-  if (p.w == DT_FP8) {
-    if ((err = run_regime<true, EPI_GELU>(regime, g1, rows_cap, st)) != hipSuccess) return err;
-    return run_regime<true, EPI_BIAS>(regime, g2, rows_cap, st);
-  }
-  if ((err = run_regime<false, EPI_GELU>(regime, g1, rows_cap, st)) != hipSuccess) return err;
-  return run_regime<false, EPI_BIAS>(regime, g2, rows_cap, st);
+static GemmArgs expert_args(const Problem& p, const int32_t* counts, const int32_t* offsets) {
+  GemmArgs g{};
+  g.offsets = offsets; g.counts = counts; g.G = p.E;
+  return g;
+}
+
+template <int EPI>
+static hipError_t run_expert_gemm(const Problem& p, const GemmArgs& g, int64_t rows_cap, hipStream_t st) {
+  if (p.act == DT_F32) return run_f32<EPI>(g, rows_cap, st);
+  if (p.w == DT_FP8) return run_regime<true, EPI>(gemm_regime(p), g, rows_cap, st);
+  return run_regime<false, EPI>(gemm_regime(p), g, rows_cap, st);
+}
+
+// h = GeLU(x_perm W1^T + b1) over the expert groups.
+hipError_t launch_expert_up(const Problem& p, int64_t rows_cap, const void* x_perm,
+                            const int32_t* counts, const int32_t* offsets, const void* W1,
+                            const void* b1, const float* s1, void* h, hipStream_t st) {
+  GemmArgs g = expert_args(p, counts, offsets);
+  g.A = x_perm; g.lda = p.d;
+  g.B = W1; g.ldb = p.d; g.b_gstride = (int64_t)p.d_ff * p.d;
+  g.scale = s1; g.bias = b1;
+  g.C = h; g.ldc = p.d_ff;
+  g.N = p.d_ff; g.K = p.d;
+  return run_expert_gemm<EPI_GELU>(p, g, rows_cap, st);
+}
+
+// y_perm = h W2^T + b2 over the expert groups.
+hipError_t launch_expert_down(const Problem& p, int64_t rows_cap, const void* h,
+                              const int32_t* counts, const int32_t* offsets, const void* W2,
+                              const void* b2, const float* s2, void* y_perm, hipStream_t st) {
+  GemmArgs g = expert_args(p, counts, offsets);
+  g.A = h; g.lda = p.d_ff;
+  g.B = W2; g.ldb = p.d_ff; g.b_gstride = (int64_t)p.d * p.d_ff;
+  g.scale = s2; g.bias = b2;
+  g.C = y_perm; g.ldc = p.d;
+  g.N = p.d; g.K = p.d_ff;
+  return run_expert_gemm<EPI_BIAS>(p, g, rows_cap, st);
 }
 
 // Router scores x W_r^T (+ router_bias) as one bf16 MFMA GEMM (E % 64 == 0).
