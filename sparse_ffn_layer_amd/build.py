@@ -11,6 +11,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -39,15 +40,39 @@ def common_flags():
             "-Wno-unused-command-line-argument"]
 
 
+def _check_no_scratch(src: str, remarks: str) -> None:
+    """Fail if a GEMM kernel uses scratch (register spills).
+
+    The GEMM kernels read their MFMA fragments with inline-asm LDS loads and
+    wait for them explicitly; a spill would copy such a register before the
+    data has arrived, so a spilling GEMM kernel is a build error, not a slow
+    kernel."""
+    name = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and "grouped_gemm_bf16_kernel" in name and int(m.group(1)) > 0:
+            raise RuntimeError(f"{src}: kernel {name} spills ({m.group(1)} scratch bytes/lane)")
+
+
 def _compile(src: str, asm: bool) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(OBJ, src + ".o")
     cmd = [hipcc(), "-x", "hip", "-c", path, "-o", obj] + common_flags()
+    if src.endswith(".hip"):
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in l and l.strip())
     if r.returncode != 0:
+        out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                        if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l and l.strip())
         raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+    _check_no_scratch(src, r.stderr)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l and l.strip()
+                    and not l.lstrip().startswith(("|", "^")) and not re.match(r"^\s*\d+ \|", l))
     if asm and src.endswith(".hip"):
         s = os.path.join(OBJ, src + ".s")
         subprocess.run([hipcc(), "-x", "hip", "-S", "--cuda-device-only", path, "-o", s] + common_flags(),

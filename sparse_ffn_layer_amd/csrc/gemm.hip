@@ -17,15 +17,29 @@
 // Rows of group g occupy [offsets[g], offsets[g] + counts[g]) and every
 // group starts at a multiple of the row tile, so a BM x BN tile never
 // straddles two experts; its expert is found by a binary search over the
-// offsets, on the device, without a host round trip.  Tiles past the last
-// group, and rows past a group's count, do no loads or stores.
+// offsets, on the device, without a host round trip.  Rows past a group's
+// count do no loads or stores.
+//
+// Scheduling: the kernel is persistent.  The number of row tiles in use is
+// read on the device (offsets[G] / BM), so the host never waits for the
+// routing.  The tile space is cut into 8 contiguous slices, one per XCD
+// (workgroups are dealt to the 8 XCDs round-robin, so workgroup b runs on
+// XCD b % 8), and inside a slice tiles are ordered in bands of GM row tiles
+// with the row tile varying fastest: the workgroups running at the same time
+// on one XCD share a few weight and activation panels through that XCD's
+// L2.  The mapping is a bijection for any grid of at least 8 workgroups;
+// only the locality depends on the dispatch order.
 //
 // gfx950 mapping: 16x16x32 bf16 MFMAs, tiles staged in LDS by the
 // global_load_lds DMA path (no VGPR staging) in a STAGES-deep ring, XOR
 // swizzled in 16-byte chunks so the fragment reads are bank-conflict free.
 // The MFMA is issued as (weights x activations) so each lane ends up with
-// four consecutive output channels of one row (one 8-byte store).
+// four consecutive output channels of one row (one 8-byte store).  Fragments
+// of the next 32-wide k step are read from LDS while the MFMAs of the
+// current one run.
 #include "common.h"
+
+#include <type_traits>
 
 namespace sfl {
 
@@ -46,7 +60,7 @@ struct GemmArgs {
   int G;
   int64_t M;
   int N, K;
-  int m_tiles, n_tiles;
+  int m_tiles, n_tiles;  // m_tiles: upper bound (capacity / BM)
 };
 
 // Find the tile's group and number of valid rows; false if it has none.
@@ -70,13 +84,37 @@ __device__ __forceinline__ bool tile_group(const GemmArgs& a, int64_t row0, int&
   return rows > 0;
 }
 
+// Row tiles in use: read on the device from the padded offsets.
+template <int BM>
+__device__ __forceinline__ int rows_tiles_used(const GemmArgs& a) {
+  if (a.offsets == nullptr) return (int)((a.M + BM - 1) / BM);
+  const int used = (a.offsets[a.G] + BM - 1) / BM;
+  return used < a.m_tiles ? used : a.m_tiles;
+}
+
 // Two OCP e4m3 codes (low 16 bits of `w` if !HI) -> two bf16, exact.
 template <bool HI>
 __device__ __forceinline__ bf16x2_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI>
+// LDS slot of 16-byte chunk c in row r of a tile with NC chunks per row is
+// c ^ swz<NC>(r).  The XOR term (r ^ (r >> 2)) keeps the 16-byte fragment
+// reads of both MFMA shapes free of bank conflicts for 64-, 128- and
+// 256-byte rows (measured on gfx950: 64 banks, ~240 B/clk per CU).
+template <int NC>
+__device__ __forceinline__ int swz(int r) {
+  return NC > 1 ? ((r ^ (r >> 2)) & (NC - 1)) : 0;
+}
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// MF selects the MFMA: 16 (v_mfma_f32_16x16x32_bf16) or 32
+// (v_mfma_f32_32x32x16_bf16).  Operand lanes: row (lane % MF) of the
+// fragment, 8 consecutive k values starting at 8 * (lane / MF).  Result
+// lanes (weights as the first operand): activation row m = lane % MF, four
+// consecutive output channels n per group of four accumulator registers.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_bf16_kernel(const GemmArgs a) {
   constexpr int NT = 64 * WM * WN;
@@ -90,12 +128,19 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   constexpr int B_LOADS = BN * CB / NT;
   constexpr int LOADS = A_LOADS + B_LOADS;
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int KS = BK / 32;  // MFMA k-steps per stage
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int KSTEP = MF == 16 ? 32 : 16;  // k per MFMA
+  constexpr int KS = BK / KSTEP;             // MFMA k-steps per stage
+  constexpr int NACC = MF == 16 ? 4 : 16;
+  typedef typename std::conditional<MF == 16, f32x4_t, f32x16_t>::type acc_t;
+  static_assert(MF == 16 || MF == 32, "MFMA shape");
   static_assert(BM * CA % NT == 0 && BN * CB % NT == 0, "tile loads must divide evenly");
-  static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+  static_assert(FM >= 1 && FN >= 1 && WTM % MF == 0 && WTN % MF == 0, "wave tile");
   static_assert((CA & (CA - 1)) == 0 && (CB & (CB - 1)) == 0, "chunk counts are powers of two");
-  static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
+  static_assert((STAGES - 1) * LOADS < 64, "vmcnt range");
+  static_assert(STAGES >= 2, "at least two stages");
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS size");
+  static_assert(!BFP8 || CB >= 1, "fp8 rows hold at least one chunk");
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
@@ -103,134 +148,250 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane % MF, lk = lane / MF;
 
-  const int bid = blockIdx.x;
-  const int mt = bid % a.m_tiles;
-  const int nt = bid / a.m_tiles;
-  const int64_t row0 = (int64_t)mt * BM;
-  int g, rows;
-  if (!tile_group<BM>(a, row0, g, rows)) return;
-  const int n0 = nt * BN;
+  // ---- persistent, XCD-sliced tile loop
+  const int m_used = rows_tiles_used<BM>(a);
+  const int64_t T = (int64_t)m_used * a.n_tiles;
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;
+  const int nx = (nwg - xcd + 7) >> 3;  // workgroups with this blockIdx % 8
+  const int64_t t_lo = T * xcd / 8, t_hi = T * (xcd + 1) / 8;
+  const int64_t band = (int64_t)GM * a.n_tiles;
 
-  // per-thread source addresses of the 16-byte chunks this thread copies
-  const char* a_src[A_LOADS];
-  const char* b_src[B_LOADS];
-  {
-    const char* A = (const char*)a.A;
+  for (int64_t L = t_lo + xj; L < t_hi; L += nx) {
+    const int64_t bnd = L / band;
+    const int first_m = (int)(bnd * GM);
+    const int gm = m_used - first_m < GM ? m_used - first_m : GM;
+    const int rem = (int)(L - bnd * band);
+    const int mt = first_m + rem % gm;
+    const int nt = rem / gm;
+    const int64_t row0 = (int64_t)mt * BM;
+    int g, rows;
+    if (!tile_group<BM>(a, row0, g, rows)) continue;
+    const int n0 = nt * BN;
+
+    // Global -> LDS copies: buffer loads with a scalar resource per tile
+    // (its base is the tile's first row / channel) and one 32-bit offset
+    // per copied chunk; the k position goes into the scalar offset.  Rows
+    // past the group's count re-read its last row and are never stored, so
+    // every access stays inside the operands.
+    const i32x4_t rsrc_a = make_rsrc((const char*)a.A + row0 * a.lda * 2, 0x7fffffffu);
+    const i32x4_t rsrc_b = make_rsrc((const char*)a.B + (int64_t)g * a.b_gstride * BSZ + (int64_t)n0 * a.ldb * BSZ,
+                                     0x7fffffffu);
+    uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int q = i * NT + tid;
       const int r = q / CA, s = q % CA;
-      const int c = s ^ (r & (CA - 1));
       const int rr = r < rows ? r : rows - 1;
-      a_src[i] = A + ((row0 + rr) * a.lda) * 2 + c * 16;
+      a_off[i] = (uint32_t)(rr * a.lda * 2 + (s ^ swz<CA>(r)) * 16);
     }
-    const char* B = (const char*)a.B + (int64_t)g * a.b_gstride * BSZ;
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       const int q = i * NT + tid;
       const int r = q / CB, s = q % CB;
-      const int c = s ^ (r & (CB - 1));
-      b_src[i] = B + ((int64_t)(n0 + r) * a.ldb) * BSZ + c * 16;
+      b_off[i] = (uint32_t)(r * a.ldb * BSZ + (s ^ swz<CB>(r)) * 16);
     }
-  }
-  auto issue = [&](int kt, int slot) {
-    char* sa = smem + slot * STAGE_BYTES;
-    char* sb = sa + A_BYTES;
-    const int64_t ka = (int64_t)kt * BK * 2, kb = (int64_t)kt * BK * BSZ;
+    auto issue = [&](int kt, int slot) {
+      char* sa = smem + slot * STAGE_BYTES;
+      char* sb = sa + A_BYTES;
+      const uint32_t ka = (uint32_t)(kt * BK * 2), kb = (uint32_t)(kt * BK * BSZ);
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) load_lds_16(a_src[i] + ka, sa + (i * NT + wave * 64) * 16);
+      for (int i = 0; i < A_LOADS; ++i)
+        buffer_load_lds_16(rsrc_a, sa + (i * NT + wave * 64) * 16, a_off[i], ka);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) load_lds_16(b_src[i] + kb, sb + (i * NT + wave * 64) * 16);
-  };
+      for (int i = 0; i < B_LOADS; ++i)
+        buffer_load_lds_16(rsrc_b, sb + (i * NT + wave * 64) * 16, b_off[i], kb);
+    };
 
-  f32x4_t acc[FM][FN];
+    // Fragment reads go through inline-asm ds_read so that the compiler does
+    // not insert its own (conservative) LDS waits: the k-step whose MFMAs
+    // run next is always waited for explicitly with lgkmcnt, after the reads
+    // of the following k-step have been issued.  Each fragment keeps one LDS
+    // address (slot 0, k-step 0); k-step ks XORs its chunk index into the
+    // chunk bits (disjoint from the lane's own chunk bits, and the slot and
+    // row parts of the address are multiples of the row size), and the slot
+    // adds a multiple of the stage size.
+    typedef typename std::conditional<BFP8, uint2, bf16x8_t>::type braw_t;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    uint32_t a_rd[FM], b_rd[FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * MF + lr;
+      a_rd[i] = lds0 + (uint32_t)(r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
+    }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int KT = a.K / BK;
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s, s);
-
-  const int lr = lane & 15, lk = lane >> 4;
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + STAGES - 2 < KT) wait_vmcnt<(STAGES - 2) * LOADS>();
-    else wait_vmcnt<0>();
-    barrier_lds();
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-
-    const char* sa = smem + (kt % STAGES) * STAGE_BYTES;
-    const char* sb = sa + A_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8_t af[FM], bfr[FN];
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WTN + j * MF + lr;
+      if constexpr (BFP8)  // this lane's 8 codes of k-step 0: bytes [8 lk, 8 lk + 8) of the row
+        b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CB * 16 + ((((lk * 8) >> 4) ^ swz<CB>(r)) << 4) + ((lk * 8) & 8));
+      else
+        b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CB * 16 + ((lk ^ swz<CB>(r)) << 4));
+    }
+    constexpr int A_KX = (KSTEP / 8) << 4;                      // chunk bits of one k-step, A and bf16 B
+    constexpr int B_KX = BFP8 ? ((KSTEP / 16) << 4) : A_KX;      // fp8 B: 16 codes per chunk
+    auto read_sub = [&](int slot, int ks, bf16x8_t (&af)[FM], braw_t (&bfr)[FN]) {
+      const uint32_t so = (uint32_t)(slot * STAGE_BYTES);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 16 + lr;
-        const int c = ks * 4 + lk;
-        af[i] = *(const bf16x8_t*)(sa + (r * CA + (c ^ (r & (CA - 1)))) * 16);
+        const uint32_t addr = (a_rd[i] ^ (uint32_t)(ks * A_KX)) + so;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(af[i]) : "v"(addr));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int r = wn * WTN + j * 16 + lr;
+        const uint32_t addr = (b_rd[j] ^ (uint32_t)(ks * B_KX)) + so;
+        if constexpr (BFP8) asm volatile("ds_read_b64 %0, %1" : "=v"(bfr[j]) : "v"(addr));
+        else asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[j]) : "v"(addr));
+      }
+    };
+    constexpr int READS = FM + FN;  // LDS reads per k-step
+
+    acc_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < NACC; ++v) acc[i][j][v] = 0.f;
+
+    auto mma_sub = [&](const bf16x8_t (&af)[FM], const braw_t (&braw)[FN]) {
+      bf16x8_t bfr[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
         if constexpr (BFP8) {
-          const int c = ks * 2 + (lk >> 1);
-          const uint2 q = *(const uint2*)(sb + (r * CB + (c ^ (r & (CB - 1)))) * 16 + (lk & 1) * 8);
+          const uint2 q = braw[j];
           const bf16x2_t p0 = fp8x2_to_bf16x2<false>(q.x), p1 = fp8x2_to_bf16x2<true>(q.x);
           const bf16x2_t p2 = fp8x2_to_bf16x2<false>(q.y), p3 = fp8x2_to_bf16x2<true>(q.y);
           bfr[j] = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
         } else {
-          const int c = ks * 4 + lk;
-          bfr[j] = *(const bf16x8_t*)(sb + (r * CB + (c ^ (r & (CB - 1)))) * 16);
+          bfr[j] = braw[j];
         }
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  // epilogue: lane holds out[m = lr][n = 4*lk .. 4*lk+3] of each 16x16 tile
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * WTN + j * 16 + lk * 4;
-    float sc[4] = {1.f, 1.f, 1.f, 1.f}, bi[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (BFP8) {
-      const float4 s4 = *(const float4*)(a.scale + (int64_t)g * a.N + n);
-      sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
-    }
-    if (a.bias != nullptr) {
-      if constexpr (EPI == EPI_F32) {
-        const float4 b4 = *(const float4*)((const float*)a.bias + (int64_t)g * a.N + n);
-        bi[0] = b4.x; bi[1] = b4.y; bi[2] = b4.z; bi[3] = b4.w;
-      } else {
-        const uint2 b2 = *(const uint2*)((const uint16_t*)a.bias + (int64_t)g * a.N + n);
-        bi[0] = bf16_bits_to_f32(b2.x & 0xffff); bi[1] = bf16_bits_to_f32(b2.x >> 16);
-        bi[2] = bf16_bits_to_f32(b2.y & 0xffff); bi[3] = bf16_bits_to_f32(b2.y >> 16);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = wm * WTM + i * 16 + lr;
-      if (m < rows) {
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float t = BFP8 ? acc[i][j][q] * sc[q] : acc[i][j][q];
-          t += bi[q];
-          if constexpr (EPI == EPI_GELU) t = gelu_erf(t);
-          v[q] = t;
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (MF == 16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
         }
-        const int64_t off = (row0 + m) * a.ldc + n;
-        if constexpr (EPI == EPI_F32) {
-          *(float4*)((float*)a.C + off) = make_float4(v[0], v[1], v[2], v[3]);
+    };
+
+    // Pipeline over k-steps (KS per stage) with two fragment buffers: the
+    // fragments of the next k-step are read from LDS while the MFMAs of the
+    // current one run.  Before the last k-step of stage kt the barrier makes
+    // stage kt+1 visible (its first k-step is prefetched across the stage
+    // boundary) and proves every wave has finished reading stage kt, whose
+    // slot is then refilled with stage kt+STAGES.
+    const int KT = a.K / BK;
+    __syncthreads();  // every wave is done with the previous tile's LDS
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < KT) issue(s, s);
+    if (KT >= STAGES) wait_vmcnt<(STAGES - 1) * LOADS>();
+    else wait_vmcnt<0>();
+    barrier_lds();
+    bf16x8_t fa[2][FM];
+    braw_t fb[2][FN];
+    read_sub(0, 0, fa[0], fb[0]);
+
+    // one stage with a successor; `p` is the buffer holding k-step 0
+    auto stage = [&](int kt, auto p_tag) {
+      constexpr int p = decltype(p_tag)::value;
+      const int slot = kt % STAGES;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = (p + ks) & 1, nxt = (p + ks + 1) & 1;
+        if (ks + 1 < KS) {
+          read_sub(slot, ks + 1, fa[nxt], fb[nxt]);
         } else {
-          *(uint2*)((uint16_t*)a.C + off) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          if (kt + STAGES - 1 < KT) wait_vmcnt<(STAGES - 2) * LOADS>();
+          else wait_vmcnt<0>();
+          barrier_lds();
+          if (kt + STAGES < KT) issue(kt + STAGES, slot);
+          read_sub((kt + 1) % STAGES, 0, fa[nxt], fb[nxt]);
+        }
+        wait_lgkmcnt<READS>();  // k-step `cur` has landed; `nxt` may be in flight
+        __builtin_amdgcn_sched_barrier(0);
+        mma_sub(fa[cur], fb[cur]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // the last stage: no successor to prefetch
+    auto last_stage = [&](int kt, auto p_tag) {
+      constexpr int p = decltype(p_tag)::value;
+      const int slot = kt % STAGES;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = (p + ks) & 1, nxt = (p + ks + 1) & 1;
+        if (ks + 1 < KS) {
+          read_sub(slot, ks + 1, fa[nxt], fb[nxt]);
+          wait_lgkmcnt<READS>();
+        } else {
+          wait_lgkmcnt<0>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma_sub(fa[cur], fb[cur]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, (KS & 1)>;
+    int kt = 0;
+    for (; kt + 2 < KT; kt += 2) {
+      stage(kt, P0{});
+      stage(kt + 1, P1{});
+    }
+    if (kt + 1 < KT) {
+      stage(kt, P0{});
+      last_stage(kt + 1, P1{});
+    } else {
+      last_stage(kt, P0{});
+    }
+
+    // epilogue: lane holds out[m][n .. n+3] for m = lane % MF and, per group
+    // q4 of four accumulators, n = (MF == 16 ? 4 * lk : 8 * q4 + 4 * lk)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int q4 = 0; q4 < NACC / 4; ++q4) {
+        const int n = n0 + wn * WTN + j * MF + q4 * 8 + lk * 4;
+        float sc[4] = {1.f, 1.f, 1.f, 1.f}, bi[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BFP8) {
+          const float4 s4 = *(const float4*)(a.scale + (int64_t)g * a.N + n);
+          sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
+        }
+        if (a.bias != nullptr) {
+          if constexpr (EPI == EPI_F32) {
+            const float4 b4 = *(const float4*)((const float*)a.bias + (int64_t)g * a.N + n);
+            bi[0] = b4.x; bi[1] = b4.y; bi[2] = b4.z; bi[3] = b4.w;
+          } else {
+            const uint2 b2 = *(const uint2*)((const uint16_t*)a.bias + (int64_t)g * a.N + n);
+            bi[0] = bf16_bits_to_f32(b2.x & 0xffff); bi[1] = bf16_bits_to_f32(b2.x >> 16);
+            bi[2] = bf16_bits_to_f32(b2.y & 0xffff); bi[3] = bf16_bits_to_f32(b2.y >> 16);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int m = wm * WTM + i * MF + lr;
+          if (m < rows) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float t = BFP8 ? acc[i][j][q4 * 4 + q] * sc[q] : acc[i][j][q4 * 4 + q];
+              t += bi[q];
+              if constexpr (EPI == EPI_GELU) t = gelu_erf(t);
+              v[q] = t;
+            }
+            const int64_t off = (row0 + m) * a.ldc + n;
+            if constexpr (EPI == EPI_F32) {
+              *(float4*)((float*)a.C + off) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              *(uint2*)((uint16_t*)a.C + off) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+          }
         }
       }
     }
@@ -297,8 +458,6 @@ __global__ void __launch_bounds__(256) grouped_gemm_f32_kernel(const GemmArgs a)
 }
 
 // ------------------------------------------------------------------ configs
-// Tile shapes per regime; the padding granule of the expert groups equals BM.
-struct TileCfg { int bm; };
 // 0: prefill (many rows per expert)  1: mid  2: decode (few rows per expert)
 int gemm_regime(const Problem& p) {
   if (p.act == DT_F32) return 3;
@@ -307,23 +466,49 @@ int gemm_regime(const Problem& p) {
   if (per_expert >= 48) return 1;
   return 2;
 }
+// Padding granule of the expert groups: the row tile of the regime.
 int gemm_tile_m(const Problem& p) {
   switch (gemm_regime(p)) {
-    case 0: return 128;
+    case 0: return 256;
     case 1: return 64;
     case 2: return 16;
     default: return 64;
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI>
-static hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st) {
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Persistent launch: as many workgroups as fit on the device at once (a
+// multiple of 8, at least 8), never more than there are tiles.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF = 16>
+hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st) {
+  auto kern = grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF>;
+  constexpr int NT = 64 * WM * WN;
   a.m_tiles = (int)ceil_div(rows_cap, BM);
   a.n_tiles = a.N / BN;
-  const int64_t blocks = (int64_t)a.m_tiles * a.n_tiles;
-  if (blocks == 0) return hipSuccess;
-  grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI>
-      <<<(unsigned)blocks, 64 * WM * WN, 0, st>>>(a);
+  const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
+  if (tiles == 0) return hipSuccess;
+  static int occ = 0;  // resident workgroups per CU (same for every gfx950 device)
+  if (occ == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NT, 0) != hipSuccess || n < 1) n = 1;
+    occ = n;
+  }
+  int64_t grid = (int64_t)device_cus() * occ;
+  if (grid > tiles) grid = tiles;
+  grid = grid < 8 ? 8 : grid / 8 * 8;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -338,20 +523,20 @@ static hipError_t run_f32(GemmArgs a, int64_t rows_cap, hipStream_t st) {
 }
 
 // Tile shapes per regime.  BN must divide N and BK must divide K; both are
-// multiples of 64, so the 128-wide variants fall back to 64 when needed.
+// multiples of 64, so the wider variants fall back when needed.
 template <bool BFP8, int EPI>
 static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hipStream_t st) {
   const bool n128 = a.N % 128 == 0, k128 = a.K % 128 == 0;
   switch (regime) {
     case 0:
-      if (n128) return run_bf16<128, 128, 64, 2, 2, 3, BFP8, EPI>(a, rows_cap, st);
-      return run_bf16<128, 64, 64, 2, 2, 3, BFP8, EPI>(a, rows_cap, st);
+      if (n128) return run_bf16<256, 128, 64, 4, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
+      return run_bf16<256, 64, 64, 4, 1, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
     case 1:
-      if (n128) return run_bf16<64, 128, 64, 1, 4, 4, BFP8, EPI>(a, rows_cap, st);
-      return run_bf16<64, 64, 64, 1, 4, 4, BFP8, EPI>(a, rows_cap, st);
+      if (n128) return run_bf16<64, 128, 64, 1, 4, 4, BFP8, EPI, 4>(a, rows_cap, st);
+      return run_bf16<64, 64, 64, 1, 4, 4, BFP8, EPI, 4>(a, rows_cap, st);
     default:
-      if (k128) return run_bf16<16, 64, 128, 1, 4, 5, BFP8, EPI>(a, rows_cap, st);
-      return run_bf16<16, 64, 64, 1, 2, 8, BFP8, EPI>(a, rows_cap, st);  // 128 threads: A tile is 128 chunks
+      if (k128) return run_bf16<16, 64, 128, 1, 4, 5, BFP8, EPI, 1>(a, rows_cap, st);
+      return run_bf16<16, 64, 64, 1, 2, 8, BFP8, EPI, 1>(a, rows_cap, st);  // 128 threads: A tile is 128 chunks
   }
 }
 
@@ -404,7 +589,7 @@ hipError_t launch_router_gemm(const Problem& p, const void* x, const void* Wr, c
   a.C = logits; a.ldc = p.E;
   a.M = p.S; a.G = 1;
   a.N = p.E; a.K = p.d;
-  return run_bf16<128, 64, 64, 4, 1, 3, false, EPI_F32>(a, p.S, st);
+  return run_bf16<128, 64, 64, 4, 1, 3, false, EPI_F32, 8>(a, p.S, st);
 }
 
 }  // namespace sfl
