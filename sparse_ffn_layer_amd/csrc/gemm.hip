@@ -133,6 +133,9 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   constexpr int KS = BK / KSTEP;             // MFMA k-steps per stage
   constexpr int NACC = MF == 16 ? 4 : 16;
   typedef typename std::conditional<MF == 16, f32x4_t, f32x16_t>::type acc_t;
+  // Large wave tiles keep their accumulators in AGPRs (MFMAs issued as
+  // inline asm with AGPR operands), leaving the VGPRs to the fragments.
+  constexpr bool AGPR_ACC = MF == 32 && !BFP8 && FM * FN * NACC > 128;
   static_assert(MF == 16 || MF == 32, "MFMA shape");
   static_assert(BM * CA % NT == 0 && BN * CB % NT == 0, "tile loads must divide evenly");
   static_assert(FM >= 1 && FN >= 1 && WTM % MF == 0 && WTN % MF == 0, "wave tile");
@@ -254,6 +257,13 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < NACC; ++v) acc[i][j][v] = 0.f;
+    if constexpr (AGPR_ACC) {
+      // the zeroed accumulators are written to AGPRs by VALU moves; give
+      // them the wait states an MFMA source-C read needs after such a write
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 4" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     auto mma_sub = [&](const bf16x8_t (&af)[FM], const braw_t (&braw)[FN]) {
       bf16x8_t bfr[FN];
@@ -272,7 +282,9 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          if constexpr (MF == 16)
+          if constexpr (AGPR_ACC)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(bfr[j]), "v"(af[i]));
+          else if constexpr (MF == 16)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
           else
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
@@ -297,37 +309,24 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     braw_t fb[2][FN];
     read_sub(0, 0, fa[0], fb[0]);
 
-    // one stage with a successor; `p` is the buffer holding k-step 0
+    // one stage; `p` is the buffer holding its k-step 0.  The last stage
+    // has no successor to prefetch (uniform branches: no divergence).
     auto stage = [&](int kt, auto p_tag) {
       constexpr int p = decltype(p_tag)::value;
       const int slot = kt % STAGES;
+      const bool more = kt + 1 < KT;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int cur = (p + ks) & 1, nxt = (p + ks + 1) & 1;
         if (ks + 1 < KS) {
           read_sub(slot, ks + 1, fa[nxt], fb[nxt]);
-        } else {
+          wait_lgkmcnt<READS>();  // k-step `cur` has landed; `nxt` may be in flight
+        } else if (more) {
           if (kt + STAGES - 1 < KT) wait_vmcnt<(STAGES - 2) * LOADS>();
           else wait_vmcnt<0>();
           barrier_lds();
           if (kt + STAGES < KT) issue(kt + STAGES, slot);
           read_sub((kt + 1) % STAGES, 0, fa[nxt], fb[nxt]);
-        }
-        wait_lgkmcnt<READS>();  // k-step `cur` has landed; `nxt` may be in flight
-        __builtin_amdgcn_sched_barrier(0);
-        mma_sub(fa[cur], fb[cur]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    // the last stage: no successor to prefetch
-    auto last_stage = [&](int kt, auto p_tag) {
-      constexpr int p = decltype(p_tag)::value;
-      const int slot = kt % STAGES;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int cur = (p + ks) & 1, nxt = (p + ks + 1) & 1;
-        if (ks + 1 < KS) {
-          read_sub(slot, ks + 1, fa[nxt], fb[nxt]);
           wait_lgkmcnt<READS>();
         } else {
           wait_lgkmcnt<0>();
@@ -339,24 +338,28 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, (KS & 1)>;
-    int kt = 0;
-    for (; kt + 2 < KT; kt += 2) {
+    for (int kt = 0; kt < KT; kt += 2) {
       stage(kt, P0{});
-      stage(kt + 1, P1{});
-    }
-    if (kt + 1 < KT) {
-      stage(kt, P0{});
-      last_stage(kt + 1, P1{});
-    } else {
-      last_stage(kt, P0{});
+      if (kt + 1 < KT) stage(kt + 1, P1{});
     }
 
+    if constexpr (AGPR_ACC) {
+      // the last MFMAs wrote the accumulators (AGPRs) behind the compiler's
+      // back: wait out the MFMA-write -> accvgpr-read hazard before the
+      // epilogue copies them
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // epilogue: lane holds out[m][n .. n+3] for m = lane % MF and, per group
     // q4 of four accumulators, n = (MF == 16 ? 4 * lk : 8 * q4 + 4 * lk)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
       for (int q4 = 0; q4 < NACC / 4; ++q4) {
+        // one group of output channels at a time: keeps the scheduler from
+        // lifting every accumulator into VGPRs at once
+        __builtin_amdgcn_sched_barrier(0);
         const int n = n0 + wn * WTN + j * MF + q4 * 8 + lk * 4;
         float sc[4] = {1.f, 1.f, 1.f, 1.f}, bi[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (BFP8) {
@@ -526,9 +529,10 @@ static hipError_t run_f32(GemmArgs a, int64_t rows_cap, hipStream_t st) {
 // multiples of 64, so the wider variants fall back when needed.
 template <bool BFP8, int EPI>
 static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hipStream_t st) {
-  const bool n128 = a.N % 128 == 0, k128 = a.K % 128 == 0;
+  const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0, k128 = a.K % 128 == 0;
   switch (regime) {
     case 0:
+      if (n256) return run_bf16<256, 256, 64, 4, 2, 2, BFP8, EPI, 4, 32>(a, rows_cap, st);
       if (n128) return run_bf16<256, 128, 64, 4, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
       return run_bf16<256, 64, 64, 4, 1, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
     case 1:
