@@ -176,19 +176,20 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
 
     // Global -> LDS copies: buffer loads with a scalar resource per tile
     // (its base is the tile's first row / channel) and one 32-bit offset
-    // per copied chunk; the k position goes into the scalar offset.  Rows
-    // past the group's count re-read its last row and are never stored, so
-    // every access stays inside the operands.
-    const i32x4_t rsrc_a = make_rsrc((const char*)a.A + row0 * a.lda * 2, 0x7fffffffu);
+    // per copied chunk; the k position goes into the scalar offset.  The
+    // resources cover exactly the tile's valid rows (num_records in bytes),
+    // so chunks of rows past the group's count are dropped by the buffer
+    // range check: no memory access, zeros in LDS, and those rows are never
+    // stored.  Every access stays inside the operands by construction.
+    const i32x4_t rsrc_a = make_rsrc((const char*)a.A + row0 * a.lda * 2, (uint32_t)((int64_t)rows * a.lda * 2));
     const i32x4_t rsrc_b = make_rsrc((const char*)a.B + (int64_t)g * a.b_gstride * BSZ + (int64_t)n0 * a.ldb * BSZ,
-                                     0x7fffffffu);
+                                     (uint32_t)((int64_t)BN * a.ldb * BSZ));
     uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int q = i * NT + tid;
       const int r = q / CA, s = q % CA;
-      const int rr = r < rows ? r : rows - 1;
-      a_off[i] = (uint32_t)(rr * a.lda * 2 + (s ^ swz<CA>(r)) * 16);
+      a_off[i] = (uint32_t)(r * a.lda * 2 + (s ^ swz<CA>(r)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
@@ -216,39 +217,50 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     // chunk bits (disjoint from the lane's own chunk bits, and the slot and
     // row parts of the address are multiples of the row size), and the slot
     // adds a multiple of the stage size.
-    typedef typename std::conditional<BFP8, uint2, bf16x8_t>::type braw_t;
+    //
+    // fp8 weights: a dot product does not depend on the order of k, so k is
+    // dealt to the MFMA k-steps in pairs.  For k-steps 2u and 2u+1 a lane of
+    // half h (= lk) holds the 16 codes at k = 2 KSTEP u + 16 h + [0, 16): the
+    // low 8 for k-step 2u, the high 8 for k-step 2u+1.  One 16-byte read per
+    // pair, the same conflict-free pattern as the bf16 reads; the activation
+    // fragments use the same k assignment (k-step 2u: chunk 2 KC u + 2 h,
+    // k-step 2u+1: the next chunk).
+    constexpr int KC = KSTEP / 8;  // 16-byte bf16 chunks per k-step
+    static_assert(!BFP8 || KS % 2 == 0, "fp8 weights pair the k-steps of a stage");
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     uint32_t a_rd[FM], b_rd[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WTM + i * MF + lr;
-      a_rd[i] = lds0 + (uint32_t)(r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
+      const int c0 = BFP8 ? 2 * lk : lk;
+      a_rd[i] = lds0 + (uint32_t)(r * CA * 16 + ((c0 ^ swz<CA>(r)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int r = wn * WTN + j * MF + lr;
-      if constexpr (BFP8)  // this lane's 8 codes of k-step 0: bytes [8 lk, 8 lk + 8) of the row
-        b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CB * 16 + ((((lk * 8) >> 4) ^ swz<CB>(r)) << 4) + ((lk * 8) & 8));
-      else
-        b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CB * 16 + ((lk ^ swz<CB>(r)) << 4));
+      b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CB * 16 + ((lk ^ swz<CB>(r)) << 4));
     }
-    constexpr int A_KX = (KSTEP / 8) << 4;                      // chunk bits of one k-step, A and bf16 B
-    constexpr int B_KX = BFP8 ? ((KSTEP / 16) << 4) : A_KX;      // fp8 B: 16 codes per chunk
-    auto read_sub = [&](int slot, int ks, bf16x8_t (&af)[FM], braw_t (&bfr)[FN]) {
+    // chunk-index XOR of k-step ks (A) and of the k-step pair u (fp8 B)
+    auto a_kx = [](int ks) -> uint32_t {
+      return (uint32_t)((BFP8 ? (2 * KC * (ks >> 1) + (ks & 1)) : (KC * ks)) << 4);
+    };
+    auto read_a = [&](int slot, int ks, bf16x8_t (&af)[FM]) {
       const uint32_t so = (uint32_t)(slot * STAGE_BYTES);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const uint32_t addr = (a_rd[i] ^ (uint32_t)(ks * A_KX)) + so;
+        const uint32_t addr = (a_rd[i] ^ a_kx(ks)) + so;
         asm volatile("ds_read_b128 %0, %1" : "=v"(af[i]) : "v"(addr));
       }
+    };
+    // bf16: the fragments of k-step q; fp8: the codes of k-step pair q
+    auto read_b = [&](int slot, int q, bf16x8_t (&bfr)[FN]) {
+      const uint32_t so = (uint32_t)(slot * STAGE_BYTES);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const uint32_t addr = (b_rd[j] ^ (uint32_t)(ks * B_KX)) + so;
-        if constexpr (BFP8) asm volatile("ds_read_b64 %0, %1" : "=v"(bfr[j]) : "v"(addr));
-        else asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[j]) : "v"(addr));
+        const uint32_t addr = (b_rd[j] ^ (uint32_t)((KC * q) << 4)) + so;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[j]) : "v"(addr));
       }
     };
-    constexpr int READS = FM + FN;  // LDS reads per k-step
 
     acc_t acc[FM][FN];
 #pragma unroll
@@ -265,21 +277,27 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    auto mma_sub = [&](const bf16x8_t (&af)[FM], const braw_t (&braw)[FN]) {
+    // MFMAs of one k-step; for fp8 weights `hi` selects the half of the
+    // pair's codes that belongs to this k-step
+    auto mma_sub = [&](const bf16x8_t (&af)[FM], const bf16x8_t (&braw)[FN], bool hi) {
       bf16x8_t bfr[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         if constexpr (BFP8) {
-          const uint2 q = braw[j];
-          const bf16x2_t p0 = fp8x2_to_bf16x2<false>(q.x), p1 = fp8x2_to_bf16x2<true>(q.x);
-          const bf16x2_t p2 = fp8x2_to_bf16x2<false>(q.y), p3 = fp8x2_to_bf16x2<true>(q.y);
+          const uint4 q4 = __builtin_bit_cast(uint4, braw[j]);
+          const uint32_t w0 = hi ? q4.z : q4.x, w1 = hi ? q4.w : q4.y;
+          const bf16x2_t p0 = fp8x2_to_bf16x2<false>(w0), p1 = fp8x2_to_bf16x2<true>(w0);
+          const bf16x2_t p2 = fp8x2_to_bf16x2<false>(w1), p3 = fp8x2_to_bf16x2<true>(w1);
           bfr[j] = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
         } else {
           bfr[j] = braw[j];
         }
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        // row fragments wholly past the group's last row do no MFMAs
+        // (uniform per wave: the tile's partly filled SIMDs finish early)
+        if (wm * WTM + i * MF >= rows) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           if constexpr (AGPR_ACC)
@@ -289,6 +307,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
           else
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
         }
+      }
     };
 
     // Pipeline over k-steps (KS per stage) with two fragment buffers: the
@@ -305,42 +324,51 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     if (KT >= STAGES) wait_vmcnt<(STAGES - 1) * LOADS>();
     else wait_vmcnt<0>();
     barrier_lds();
-    bf16x8_t fa[2][FM];
-    braw_t fb[2][FN];
-    read_sub(0, 0, fa[0], fb[0]);
+    // A fragments alternate per k-step; B fragments per k-step (bf16) or per
+    // k-step pair (fp8).  Buffer parities of a stage's k-step 0 come in as
+    // compile-time tags (stages are unrolled by two).
+    bf16x8_t fa[2][FM], fb[2][FN];
+    read_a(0, 0, fa[0]);
+    read_b(0, 0, fb[0]);
 
-    // one stage; `p` is the buffer holding its k-step 0.  The last stage
-    // has no successor to prefetch (uniform branches: no divergence).
-    auto stage = [&](int kt, auto p_tag) {
-      constexpr int p = decltype(p_tag)::value;
+    auto stage = [&](int kt, auto pa_tag, auto pb_tag) {
+      constexpr int pa = decltype(pa_tag)::value, pb = decltype(pb_tag)::value;
       const int slot = kt % STAGES;
       const bool more = kt + 1 < KT;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int cur = (p + ks) & 1, nxt = (p + ks + 1) & 1;
+        const int acur = (pa + ks) & 1, anxt = (pa + ks + 1) & 1;
+        const int bcur = BFP8 ? ((pb + (ks >> 1)) & 1) : ((pb + ks) & 1);
+        const int bnxt = BFP8 ? ((pb + ((ks + 1) >> 1)) & 1) : ((pb + ks + 1) & 1);
+        // does the next k-step start a new B fragment set?
+        const bool nb = BFP8 ? ((ks + 1) % 2 == 0) : true;
         if (ks + 1 < KS) {
-          read_sub(slot, ks + 1, fa[nxt], fb[nxt]);
-          wait_lgkmcnt<READS>();  // k-step `cur` has landed; `nxt` may be in flight
+          read_a(slot, ks + 1, fa[anxt]);
+          if (nb) read_b(slot, BFP8 ? (ks + 1) / 2 : ks + 1, fb[bnxt]);
+          if (nb) wait_lgkmcnt<FM + FN>();  // k-step ks has landed; the next may be in flight
+          else wait_lgkmcnt<FM>();
         } else if (more) {
           if (kt + STAGES - 1 < KT) wait_vmcnt<(STAGES - 2) * LOADS>();
           else wait_vmcnt<0>();
           barrier_lds();
           if (kt + STAGES < KT) issue(kt + STAGES, slot);
-          read_sub((kt + 1) % STAGES, 0, fa[nxt], fb[nxt]);
-          wait_lgkmcnt<READS>();
+          read_a((kt + 1) % STAGES, 0, fa[anxt]);
+          read_b((kt + 1) % STAGES, 0, fb[bnxt]);
+          wait_lgkmcnt<FM + FN>();
         } else {
           wait_lgkmcnt<0>();
         }
         __builtin_amdgcn_sched_barrier(0);
-        mma_sub(fa[cur], fb[cur]);
+        mma_sub(fa[acur], fb[bcur], BFP8 && (ks & 1));
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, (KS & 1)>;
+    using PA1 = std::integral_constant<int, (KS & 1)>;
+    using PB1 = std::integral_constant<int, BFP8 ? ((KS / 2) & 1) : (KS & 1)>;
     for (int kt = 0; kt < KT; kt += 2) {
-      stage(kt, P0{});
-      if (kt + 1 < KT) stage(kt + 1, P1{});
+      stage(kt, P0{}, P0{});
+      if (kt + 1 < KT) stage(kt + 1, PA1{}, PB1{});
     }
 
     if constexpr (AGPR_ACC) {
@@ -378,6 +406,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
+          if (wm * WTM + i * MF >= rows) continue;  // uniform: fragment wholly past the rows
           const int m = wm * WTM + i * MF + lr;
           if (m < rows) {
             float v[4];
@@ -466,14 +495,14 @@ int gemm_regime(const Problem& p) {
   if (p.act == DT_F32) return 3;
   const int64_t per_expert = p.S * p.K / p.E;
   if (per_expert >= 256) return 0;
-  if (per_expert >= 48) return 1;
+  if (per_expert >= 64) return 1;
   return 2;
 }
 // Padding granule of the expert groups: the row tile of the regime.
 int gemm_tile_m(const Problem& p) {
   switch (gemm_regime(p)) {
     case 0: return 256;
-    case 1: return 64;
+    case 1: return 128;
     case 2: return 16;
     default: return 64;
   }
@@ -536,8 +565,9 @@ static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hi
       if (n128) return run_bf16<256, 128, 64, 4, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
       return run_bf16<256, 64, 64, 4, 1, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
     case 1:
-      if (n128) return run_bf16<64, 128, 64, 1, 4, 4, BFP8, EPI, 4>(a, rows_cap, st);
-      return run_bf16<64, 64, 64, 1, 4, 4, BFP8, EPI, 4>(a, rows_cap, st);
+      if (n256) return run_bf16<128, 256, 64, 2, 4, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
+      if (n128) return run_bf16<128, 128, 64, 2, 4, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
+      return run_bf16<128, 64, 64, 2, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
     default:
       if (k128) return run_bf16<16, 64, 128, 1, 4, 5, BFP8, EPI, 1>(a, rows_cap, st);
       return run_bf16<16, 64, 64, 1, 2, 8, BFP8, EPI, 1>(a, rows_cap, st);  // 128 threads: A tile is 128 chunks
