@@ -64,6 +64,7 @@ class Workload:
         self.gate = torch.empty((c.S, c.K), dtype=torch.float32, device=dev)
         self.ws_route = M.workspace(self.p, M.STAGE_ROUTE, dev)
         self.ws_perm = M.workspace(self.p, M.STAGE_PERMUTE, dev)
+        self.ws_ffn = M.workspace(self.p, M.STAGE_EXPERT_FFN, dev)
         self.offsets = torch.empty(c.E + 1, **i32)
         self.perm = torch.empty(c.S * c.K, **i32)
         self.inv = torch.empty(c.S * c.K, **i32)
@@ -86,9 +87,9 @@ class Workload:
             "permute": lambda: M.moe_permute(p, self.idx, i["x"], self.counts, self.offsets, self.perm,
                                              self.inv, self.x_perm, ws=self.ws_perm),
             "expert_up": lambda: M.moe_expert_up(p, self.x_perm, self.counts, self.offsets, i["W1"], i["b1"],
-                                                 i["w1_scale"], h=self.h),
+                                                 i["w1_scale"], h=self.h, ws=self.ws_ffn),
             "expert_down": lambda: M.moe_expert_down(p, self.h, self.counts, self.offsets, i["W2"], i["b2"],
-                                                     i["w2_scale"], y_perm=self.y_perm),
+                                                     i["w2_scale"], y_perm=self.y_perm, ws=self.ws_ffn),
             "combine": lambda: M.moe_combine(p, self.y_perm, self.inv, self.gate, y=self.y2),
         }
 

@@ -159,7 +159,12 @@ int32_t moe_permute(const moe_problem* p, const int32_t* topk_idx, const void* x
  *   expert_counts, expert_offsets: as produced by moe_permute for this p.
  *   w1_scale, w2_scale: required for MOE_FP8_E4M3 weights, else ignored.
  *   h [rows_capacity][d_ff], y_perm [rows_capacity][d].
- *   ws: moe_workspace_bytes(p, MOE_STAGE_EXPERT_FFN) bytes (may be 0). */
+ *   ws: moe_workspace_bytes(p, MOE_STAGE_EXPERT_FFN) bytes, or NULL / fewer
+ *       bytes.  With the full workspace the last, partly filled round of
+ *       tiles of a GEMM is split along k over idle compute units (float32
+ *       partial sums, reduced in a fixed order by a second kernel: results
+ *       stay deterministic); without it the call runs unsplit.  Results of
+ *       the two modes can differ in the last float32 bits. */
 int32_t moe_expert_ffn(const moe_problem* p, const void* x_perm,
                        const int32_t* expert_counts, const int32_t* expert_offsets,
                        const void* W1, const void* b1, const void* W2, const void* b2,
@@ -169,13 +174,16 @@ int32_t moe_expert_ffn(const moe_problem* p, const void* x_perm,
 /* The two halves of moe_expert_ffn, for callers that schedule them apart:
  *   moe_expert_up:   h[r]      = GeLU(x_perm[r] W1_e + b1_e)
  *   moe_expert_down: y_perm[r] = h[r] W2_e + b2_e
- * Arguments as for moe_expert_ffn (w1_scale / w2_scale required for fp8). */
+ * Arguments as for moe_expert_ffn (w1_scale / w2_scale required for fp8);
+ * ws / ws_bytes as for moe_expert_ffn (nullable; may be shared by the two
+ * calls when they run in order on one stream). */
 int32_t moe_expert_up(const moe_problem* p, const void* x_perm, const int32_t* expert_counts,
                       const int32_t* expert_offsets, const void* W1, const void* b1,
-                      const float* w1_scale, void* h, void* stream);
+                      const float* w1_scale, void* h, void* ws, size_t ws_bytes, void* stream);
 int32_t moe_expert_down(const moe_problem* p, const void* h, const int32_t* expert_counts,
                         const int32_t* expert_offsets, const void* W2, const void* b2,
-                        const float* w2_scale, void* y_perm, void* stream);
+                        const float* w2_scale, void* y_perm, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Combine (chapter 11 sections 11.1.1 and 11.2.1; "MoE 混合专家推理", one
  * MoE forward): y[t] = sum over k = 0..K-1, in slot order, of

@@ -63,8 +63,8 @@ _SIGS = {
     "moe_route": (_i32, [_P] + [_vp] * 8 + [_vp, _sz, _vp]),
     "moe_permute": (_i32, [_P] + [_vp] * 7 + [_vp, _sz, _vp]),
     "moe_expert_ffn": (_i32, [_P] + [_vp] * 11 + [_vp, _sz, _vp]),
-    "moe_expert_up": (_i32, [_P] + [_vp] * 7 + [_vp]),
-    "moe_expert_down": (_i32, [_P] + [_vp] * 7 + [_vp]),
+    "moe_expert_up": (_i32, [_P] + [_vp] * 7 + [_vp, _sz, _vp]),
+    "moe_expert_down": (_i32, [_P] + [_vp] * 7 + [_vp, _sz, _vp]),
     "moe_combine": (_i32, [_P] + [_vp] * 4 + [_vp]),
     "moe_layer_forward": (_i32, [_P] + [_vp] * 15 + [_vp, _sz, _vp]),
 }
@@ -182,20 +182,28 @@ def moe_expert_ffn(p, x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, w1_
     return h, y_perm
 
 
-def moe_expert_up(p, x_perm, expert_counts, expert_offsets, W1, b1, w1_scale=None, h=None, stream=None):
+def moe_expert_up(p, x_perm, expert_counts, expert_offsets, W1, b1, w1_scale=None, h=None, ws=None,
+                  stream=None):
     if h is None:
         h = torch.empty((moe_rows_capacity(p), p.d_ff), dtype=_act(p), device=x_perm.device)
+    if ws is None:
+        ws = workspace(p, STAGE_EXPERT_FFN, x_perm.device)
     st = lib().moe_expert_up(ctypes.byref(p), _ptr(x_perm), _ptr(expert_counts), _ptr(expert_offsets),
-                             _ptr(W1), _ptr(b1), _ptr(w1_scale), _ptr(h), _stream(stream))
+                             _ptr(W1), _ptr(b1), _ptr(w1_scale), _ptr(h), _ptr(ws), ws.numel(),
+                             _stream(stream))
     _check("moe_expert_up", st)
     return h
 
 
-def moe_expert_down(p, h, expert_counts, expert_offsets, W2, b2, w2_scale=None, y_perm=None, stream=None):
+def moe_expert_down(p, h, expert_counts, expert_offsets, W2, b2, w2_scale=None, y_perm=None, ws=None,
+                    stream=None):
     if y_perm is None:
         y_perm = torch.empty((moe_rows_capacity(p), p.d), dtype=_act(p), device=h.device)
+    if ws is None:
+        ws = workspace(p, STAGE_EXPERT_FFN, h.device)
     st = lib().moe_expert_down(ctypes.byref(p), _ptr(h), _ptr(expert_counts), _ptr(expert_offsets),
-                               _ptr(W2), _ptr(b2), _ptr(w2_scale), _ptr(y_perm), _stream(stream))
+                               _ptr(W2), _ptr(b2), _ptr(w2_scale), _ptr(y_perm), _ptr(ws), ws.numel(),
+                               _stream(stream))
     _check("moe_expert_down", st)
     return y_perm
 

@@ -21,10 +21,12 @@ hipError_t launch_permute(const Problem&, int, const int32_t*, const void*, int3
                           int32_t*, int32_t*, void*, int32_t*, hipStream_t);
 size_t permute_scratch_ints(int64_t pairs, int E);
 hipError_t launch_expert_up(const Problem&, int64_t, const void*, const int32_t*, const int32_t*,
-                            const void*, const void*, const float*, void*, hipStream_t);
+                            const void*, const void*, const float*, void*, float*, size_t,
+                            hipStream_t);
 hipError_t launch_expert_down(const Problem&, int64_t, const void*, const int32_t*,
                               const int32_t*, const void*, const void*, const float*, void*,
-                              hipStream_t);
+                              float*, size_t, hipStream_t);
+size_t expert_split_bytes(const Problem& p);
 hipError_t launch_combine(const Problem&, const void*, const int32_t*, const float*, void*,
                           hipStream_t);
 int gemm_tile_m(const Problem& p);
@@ -88,6 +90,7 @@ size_t permute_ws(const Problem& p) { return align_up(permute_scratch_ints(p.S *
 struct LayerWs {
   float* logits; int32_t* idx; float* gate; int32_t* counts; int32_t* offsets;
   int32_t* perm; int32_t* inv; int32_t* pscratch; void* x_perm; void* h; void* y_perm;
+  float* split; size_t split_bytes;
   size_t bytes;
 };
 LayerWs layer_layout(const Problem& p, char* base) {
@@ -106,23 +109,37 @@ LayerWs layer_layout(const Problem& p, char* base) {
   w.x_perm = take((size_t)cap * p.d * act_size(p));
   w.h = take((size_t)cap * p.d_ff * act_size(p));
   w.y_perm = take((size_t)cap * p.d * act_size(p));
+  w.split_bytes = expert_split_bytes(p);
+  w.split = (float*)take(w.split_bytes);
   w.bytes = off;
   return w;
 }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// split: float32 workspace for the split-K tail (nullable; then no split).
 int32_t do_expert_ffn(const Problem& p, const void* x_perm, const int32_t* counts,
                       const int32_t* offsets, const void* W1, const void* b1, const void* W2,
                       const void* b2, const float* s1, const float* s2, void* h, void* y_perm,
-                      hipStream_t st) {
+                      float* split, size_t split_bytes, hipStream_t st) {
   const bool fp8 = p.w == DT_FP8;
   const int64_t cap = rows_capacity(p);
   int32_t s = hip_status(launch_expert_up(p, cap, x_perm, counts, offsets, W1, b1, fp8 ? s1 : nullptr,
-                                          h, st));
+                                          h, split, split_bytes, st));
   if (s != MOE_OK) return s;
   return hip_status(launch_expert_down(p, cap, h, counts, offsets, W2, b2, fp8 ? s2 : nullptr,
-                                       y_perm, st));
+                                       y_perm, split, split_bytes, st));
+}
+
+// The split-K workspace inside a caller's buffer (aligned start), or null.
+float* split_region(void* ws, size_t ws_bytes, size_t* usable) {
+  *usable = 0;
+  if (ws == nullptr) return nullptr;
+  const uintptr_t b = ((uintptr_t)ws + kAlign - 1) / kAlign * kAlign;
+  const size_t skip = b - (uintptr_t)ws;
+  if (ws_bytes <= skip) return nullptr;
+  *usable = ws_bytes - skip;
+  return (float*)b;
 }
 
 // Common checks of the expert-GEMM entry points.
@@ -184,7 +201,7 @@ size_t moe_workspace_bytes(const moe_problem* mp, int32_t stage) {
   switch (stage) {
     case MOE_STAGE_ROUTE: return route_ws(p);
     case MOE_STAGE_PERMUTE: return permute_ws(p);
-    case MOE_STAGE_EXPERT_FFN: return 0;
+    case MOE_STAGE_EXPERT_FFN: return expert_split_bytes(p) ? expert_split_bytes(p) + kAlign : 0;
     case MOE_STAGE_COMBINE: return 0;
     case MOE_STAGE_LAYER: return layer_layout(p, nullptr).bytes;
     default: return 0;
@@ -229,35 +246,41 @@ int32_t moe_expert_ffn(const moe_problem* mp, const void* x_perm, const int32_t*
                        const void* W2, const void* b2, const float* w1_scale,
                        const float* w2_scale, void* h, void* y_perm, void* ws, size_t ws_bytes,
                        void* stream) {
-  (void)ws; (void)ws_bytes;
   Problem p;
   int32_t s = check_expert(mp, &p, {x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, h, y_perm},
                            w1_scale);
   if (s != MOE_OK || p.S == 0) return s;
   if (p.w == DT_FP8 && w2_scale == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned16(w2_scale)) return MOE_ERR_INVALID_ARG;
+  size_t usable = 0;
+  float* split = split_region(ws, ws_bytes, &usable);
   return do_expert_ffn(p, x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, w1_scale, w2_scale,
-                       h, y_perm, (hipStream_t)stream);
+                       h, y_perm, split, usable, (hipStream_t)stream);
 }
 
 int32_t moe_expert_up(const moe_problem* mp, const void* x_perm, const int32_t* expert_counts,
                       const int32_t* expert_offsets, const void* W1, const void* b1,
-                      const float* w1_scale, void* h, void* stream) {
+                      const float* w1_scale, void* h, void* ws, size_t ws_bytes, void* stream) {
   Problem p;
   int32_t s = check_expert(mp, &p, {x_perm, expert_counts, expert_offsets, W1, b1, h}, w1_scale);
   if (s != MOE_OK || p.S == 0) return s;
+  size_t usable = 0;
+  float* split = split_region(ws, ws_bytes, &usable);
   return hip_status(launch_expert_up(p, rows_capacity(p), x_perm, expert_counts, expert_offsets, W1,
-                                     b1, p.w == DT_FP8 ? w1_scale : nullptr, h, (hipStream_t)stream));
+                                     b1, p.w == DT_FP8 ? w1_scale : nullptr, h, split, usable,
+                                     (hipStream_t)stream));
 }
 
 int32_t moe_expert_down(const moe_problem* mp, const void* h, const int32_t* expert_counts,
                         const int32_t* expert_offsets, const void* W2, const void* b2,
-                        const float* w2_scale, void* y_perm, void* stream) {
+                        const float* w2_scale, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
   Problem p;
   int32_t s = check_expert(mp, &p, {h, expert_counts, expert_offsets, W2, b2, y_perm}, w2_scale);
   if (s != MOE_OK || p.S == 0) return s;
+  size_t usable = 0;
+  float* split = split_region(ws, ws_bytes, &usable);
   return hip_status(launch_expert_down(p, rows_capacity(p), h, expert_counts, expert_offsets, W2, b2,
-                                       p.w == DT_FP8 ? w2_scale : nullptr, y_perm,
+                                       p.w == DT_FP8 ? w2_scale : nullptr, y_perm, split, usable,
                                        (hipStream_t)stream));
 }
 
@@ -305,7 +328,7 @@ int32_t moe_layer_forward(const moe_problem* mp, const void* x, const void* W_r,
                                 w.x_perm, w.pscratch, st));
   if (s != MOE_OK) return s;
   s = do_expert_ffn(p, w.x_perm, counts, w.offsets, W1, b1, W2, b2, w1_scale, w2_scale, w.h,
-                    w.y_perm, st);
+                    w.y_perm, w.split, w.split_bytes, st);
   if (s != MOE_OK) return s;
   return hip_status(launch_combine(p, w.y_perm, w.inv, gate, y, st));
 }

@@ -61,7 +61,33 @@ struct GemmArgs {
   int64_t M;
   int N, K;
   int m_tiles, n_tiles;  // m_tiles: upper bound (capacity / BM)
+  float* partial;        // split-K partial sums of the tail tiles ([grid][BM*BN] floats) or null
+  int grid;              // workgroups of the persistent launch
 };
+
+// Tail split of one XCD's tile range.  The tile space is cut into 8 slices
+// (one per XCD) and each slice is processed in rounds by its nx workgroups.
+// When the last round is partial (tail tiles < nx), each tail tile's k range
+// is split into `split` slices run by otherwise idle workgroups: the item
+// (tile tau, slice sig) goes to workgroup xj = tau * split + sig of that XCD,
+// which writes float32 partial sums; a second kernel adds them up in slice
+// order (deterministic) and runs the epilogue.
+struct TailPlan {
+  int64_t t_lo, t_hi, full_end;  // [t_lo, full_end): whole rounds; full_end + tau: tail tiles
+  int tail, split;               // split == 0: no split
+};
+__device__ __forceinline__ TailPlan tail_plan(int64_t T, int xcd, int nx, bool enable) {
+  TailPlan t;
+  t.t_lo = T * xcd / 8;
+  t.t_hi = T * (xcd + 1) / 8;
+  const int64_t tx = t.t_hi - t.t_lo;
+  t.full_end = t.t_lo + tx / nx * nx;
+  t.tail = (int)(tx % nx);
+  t.split = (enable && t.tail > 0) ? nx / t.tail : 0;
+  if (t.split < 2) t.split = 0;
+  if (t.split > 8) t.split = 8;
+  return t;
+}
 
 // Find the tile's group and number of valid rows; false if it has none.
 template <int BM>
@@ -108,6 +134,79 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// Tile L of the persistent order: bands of GM row tiles, the row tile varying
+// fastest inside a band.  False if the tile has no valid rows.
+template <int BM, int BN, int GM>
+__device__ __forceinline__ bool tile_coords(const GemmArgs& a, int m_used, int64_t L, int64_t& row0, int& n0,
+                                            int& g, int& rows) {
+  const int64_t band = (int64_t)GM * a.n_tiles;
+  const int64_t bnd = L / band;
+  const int first_m = (int)(bnd * GM);
+  const int gm = m_used - first_m < GM ? m_used - first_m : GM;
+  const int rem = (int)(L - bnd * band);
+  const int mt = first_m + rem % gm;
+  const int nt = rem / gm;
+  row0 = (int64_t)mt * BM;
+  n0 = nt * BN;
+  return tile_group<BM>(a, row0, g, rows);
+}
+
+// Epilogue of one tile: lane holds out[m][n .. n+3] for m = lane % MF and,
+// per group q4 of four accumulators, n = (MF == 16 ? 4 * lk : 8 * q4 + 4 * lk);
+// scale (fp8), bias, optional exact GeLU, round, store the valid rows.
+template <int BN, int WM, int WN, bool BFP8, int EPI, int MF, int FM, int FN, int NACC, typename acc_t>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const acc_t (&acc)[FM][FN], int g, int rows,
+                                              int64_t row0, int n0, int wm, int wn, int lr, int lk) {
+  constexpr int WTN = BN / WN;
+  const int WTM = FM * MF;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+#pragma unroll
+    for (int q4 = 0; q4 < NACC / 4; ++q4) {
+      // one group of output channels at a time: keeps the scheduler from
+      // lifting every accumulator into VGPRs at once
+      __builtin_amdgcn_sched_barrier(0);
+      const int n = n0 + wn * WTN + j * MF + q4 * 8 + lk * 4;
+      float sc[4] = {1.f, 1.f, 1.f, 1.f}, bi[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BFP8) {
+        const float4 s4 = *(const float4*)(a.scale + (int64_t)g * a.N + n);
+        sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
+      }
+      if (a.bias != nullptr) {
+        if constexpr (EPI == EPI_F32) {
+          const float4 b4 = *(const float4*)((const float*)a.bias + (int64_t)g * a.N + n);
+          bi[0] = b4.x; bi[1] = b4.y; bi[2] = b4.z; bi[3] = b4.w;
+        } else {
+          const uint2 b2 = *(const uint2*)((const uint16_t*)a.bias + (int64_t)g * a.N + n);
+          bi[0] = bf16_bits_to_f32(b2.x & 0xffff); bi[1] = bf16_bits_to_f32(b2.x >> 16);
+          bi[2] = bf16_bits_to_f32(b2.y & 0xffff); bi[3] = bf16_bits_to_f32(b2.y >> 16);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if (wm * WTM + i * MF >= rows) continue;  // uniform: fragment wholly past the rows
+        const int m = wm * WTM + i * MF + lr;
+        if (m < rows) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float t = BFP8 ? acc[i][j][q4 * 4 + q] * sc[q] : acc[i][j][q4 * 4 + q];
+            t += bi[q];
+            if constexpr (EPI == EPI_GELU) t = gelu_erf(t);
+            v[q] = t;
+          }
+          const int64_t off = (row0 + m) * a.ldc + n;
+          if constexpr (EPI == EPI_F32) {
+            *(float4*)((float*)a.C + off) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            *(uint2*)((uint16_t*)a.C + off) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          }
+        }
+      }
+    }
+  }
+}
 
 // MF selects the MFMA: 16 (v_mfma_f32_16x16x32_bf16) or 32
 // (v_mfma_f32_32x32x16_bf16).  Operand lanes: row (lane % MF) of the
@@ -159,20 +258,15 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;
   const int nx = (nwg - xcd + 7) >> 3;  // workgroups with this blockIdx % 8
-  const int64_t t_lo = T * xcd / 8, t_hi = T * (xcd + 1) / 8;
-  const int64_t band = (int64_t)GM * a.n_tiles;
+  const int KT_ALL = a.K / BK;
+  const TailPlan tp = tail_plan(T, xcd, nx, a.partial != nullptr && KT_ALL >= 16);
 
-  for (int64_t L = t_lo + xj; L < t_hi; L += nx) {
-    const int64_t bnd = L / band;
-    const int first_m = (int)(bnd * GM);
-    const int gm = m_used - first_m < GM ? m_used - first_m : GM;
-    const int rem = (int)(L - bnd * band);
-    const int mt = first_m + rem % gm;
-    const int nt = rem / gm;
-    const int64_t row0 = (int64_t)mt * BM;
-    int g, rows;
-    if (!tile_group<BM>(a, row0, g, rows)) continue;
-    const int n0 = nt * BN;
+  // one tile: k-tiles [kt0, kt1); part != null: store the raw float32
+  // accumulators there (a split-K slice) instead of running the epilogue
+  auto run_tile = [&](int64_t L, int kt0, int kt1, float* part) {
+    int64_t row0;
+    int n0, g, rows;
+    if (!tile_coords<BM, BN, GM>(a, m_used, L, row0, n0, g, rows)) return;
 
     // Global -> LDS copies: buffer loads with a scalar resource per tile
     // (its base is the tile's first row / channel) and one 32-bit offset
@@ -197,16 +291,19 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
       const int r = q / CB, s = q % CB;
       b_off[i] = (uint32_t)(r * a.ldb * BSZ + (s ^ swz<CB>(r)) * 16);
     }
-    auto issue = [&](int kt, int slot) {
+    // copy l of a stage: the A chunks first, then the B chunks
+    auto issue_one = [&](int kt, int slot, int l) {
       char* sa = smem + slot * STAGE_BYTES;
       char* sb = sa + A_BYTES;
-      const uint32_t ka = (uint32_t)(kt * BK * 2), kb = (uint32_t)(kt * BK * BSZ);
+      if (l < A_LOADS)
+        buffer_load_lds_16(rsrc_a, sa + (l * NT + wave * 64) * 16, a_off[l], (uint32_t)((kt0 + kt) * BK * 2));
+      else
+        buffer_load_lds_16(rsrc_b, sb + ((l - A_LOADS) * NT + wave * 64) * 16, b_off[l - A_LOADS],
+                           (uint32_t)((kt0 + kt) * BK * BSZ));
+    };
+    auto issue = [&](int kt, int slot) {
 #pragma unroll
-      for (int i = 0; i < A_LOADS; ++i)
-        buffer_load_lds_16(rsrc_a, sa + (i * NT + wave * 64) * 16, a_off[i], ka);
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i)
-        buffer_load_lds_16(rsrc_b, sb + (i * NT + wave * 64) * 16, b_off[i], kb);
+      for (int l = 0; l < LOADS; ++l) issue_one(kt, slot, l);
     };
 
     // Fragment reads go through inline-asm ds_read so that the compiler does
@@ -279,6 +376,8 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
 
     // MFMAs of one k-step; for fp8 weights `hi` selects the half of the
     // pair's codes that belongs to this k-step
+    // MFMAs of one k-step; for fp8 weights `hi` selects the half of the
+    // pair's codes that belongs to this k-step
     auto mma_sub = [&](const bf16x8_t (&af)[FM], const bf16x8_t (&braw)[FN], bool hi) {
       bf16x8_t bfr[FN];
 #pragma unroll
@@ -316,7 +415,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     // stage kt+1 visible (its first k-step is prefetched across the stage
     // boundary) and proves every wave has finished reading stage kt, whose
     // slot is then refilled with stage kt+STAGES.
-    const int KT = a.K / BK;
+    const int KT = kt1 - kt0;
     __syncthreads();  // every wave is done with the previous tile's LDS
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
@@ -379,55 +478,111 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     }
-    // epilogue: lane holds out[m][n .. n+3] for m = lane % MF and, per group
-    // q4 of four accumulators, n = (MF == 16 ? 4 * lk : 8 * q4 + 4 * lk)
+    if (part != nullptr) {
+      // split-K slice: raw accumulators in 16-byte groups, group-major so
+      // consecutive threads store consecutive 16 bytes
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int q4 = 0; q4 < NACC / 4; ++q4) {
-        // one group of output channels at a time: keeps the scheduler from
-        // lifting every accumulator into VGPRs at once
-        __builtin_amdgcn_sched_barrier(0);
-        const int n = n0 + wn * WTN + j * MF + q4 * 8 + lk * 4;
-        float sc[4] = {1.f, 1.f, 1.f, 1.f}, bi[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BFP8) {
-          const float4 s4 = *(const float4*)(a.scale + (int64_t)g * a.N + n);
-          sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
-        }
-        if (a.bias != nullptr) {
-          if constexpr (EPI == EPI_F32) {
-            const float4 b4 = *(const float4*)((const float*)a.bias + (int64_t)g * a.N + n);
-            bi[0] = b4.x; bi[1] = b4.y; bi[2] = b4.z; bi[3] = b4.w;
-          } else {
-            const uint2 b2 = *(const uint2*)((const uint16_t*)a.bias + (int64_t)g * a.N + n);
-            bi[0] = bf16_bits_to_f32(b2.x & 0xffff); bi[1] = bf16_bits_to_f32(b2.x >> 16);
-            bi[2] = bf16_bits_to_f32(b2.y & 0xffff); bi[3] = bf16_bits_to_f32(b2.y >> 16);
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < NACC; v += 4) {
+            const int q = ((i * FN + j) * NACC + v) / 4;
+            *(float4*)(part + ((size_t)q * NT + tid) * 4) =
+                make_float4(acc[i][j][v], acc[i][j][v + 1], acc[i][j][v + 2], acc[i][j][v + 3]);
           }
-        }
+      return;
+    }
+    gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
+  };
+
+  // whole tiles of the full rounds, then (with a split) this workgroup's
+  // slice of a tail tile; one call site keeps the tile body inlined once
+  const int64_t loop_end = tp.split ? tp.full_end : tp.t_hi;
+  const bool has_slice = tp.split && xj < tp.tail * tp.split;
+  for (int64_t L = tp.t_lo + xj;; L += nx) {
+    int kt0 = 0, kt1 = KT_ALL;
+    float* part = nullptr;
+    int64_t Lt = L;
+    if (L >= loop_end) {
+      if (!has_slice || L - nx >= loop_end) break;  // the slice comes once, right after the last whole tile
+      const int tau = xj / tp.split, sig = xj % tp.split;
+      Lt = tp.full_end + tau;
+      kt0 = KT_ALL * sig / tp.split;
+      kt1 = KT_ALL * (sig + 1) / tp.split;
+      part = a.partial + (size_t)blockIdx.x * (BM * BN);
+    }
+    run_tile(Lt, kt0, kt1, part);
+  }
+}
+
+// Second pass of the tail split: adds the float32 partial sums of each
+// split tile in slice order and runs the epilogue.  Same launch shape as the
+// GEMM (it recomputes the same tail plan); workgroups without a tail tile
+// return at once.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF>
+__global__ void __launch_bounds__(64 * WM * WN)
+grouped_gemm_fixup_kernel(const GemmArgs a) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int NACC = MF == 16 ? 4 : 16;
+  typedef typename std::conditional<MF == 16, f32x4_t, f32x16_t>::type acc_t;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane % MF, lk = lane / MF;
+  const int m_used = rows_tiles_used<BM>(a);
+  const int64_t T = (int64_t)m_used * a.n_tiles;
+  const int nwg = a.grid;
+  const int xcd = blockIdx.x & 7, tau = blockIdx.x >> 3;
+  const int nx = (nwg - xcd + 7) >> 3;
+  if (a.partial == nullptr || a.K / BK < 16) return;
+  const TailPlan tp = tail_plan(T, xcd, nx, true);
+  if (tp.split == 0 || tau >= tp.tail) return;
+  int64_t row0;
+  int n0, g, rows;
+  if (!tile_coords<BM, BN, GM>(a, m_used, tp.full_end + tau, row0, n0, g, rows)) return;
+  acc_t acc[FM][FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          if (wm * WTM + i * MF >= rows) continue;  // uniform: fragment wholly past the rows
-          const int m = wm * WTM + i * MF + lr;
-          if (m < rows) {
-            float v[4];
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float t = BFP8 ? acc[i][j][q4 * 4 + q] * sc[q] : acc[i][j][q4 * 4 + q];
-              t += bi[q];
-              if constexpr (EPI == EPI_GELU) t = gelu_erf(t);
-              v[q] = t;
-            }
-            const int64_t off = (row0 + m) * a.ldc + n;
-            if constexpr (EPI == EPI_F32) {
-              *(float4*)((float*)a.C + off) = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-              *(uint2*)((uint16_t*)a.C + off) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            }
-          }
-        }
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < NACC; ++v) acc[i][j][v] = 0.f;
+  // slice sums in slice order, 16-byte loads: per slice a batch of up to
+  // 16 groups (64 values) of this thread is loaded at once
+  constexpr int NQ = FM * FN * NACC / 4;  // 16-byte groups per thread
+  constexpr int QB = NQ < 16 ? NQ : 16;
+  static_assert(NQ % QB == 0, "group batches");
+  float4 sum[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) sum[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q0 = 0; q0 < NQ; q0 += QB) {
+    for (int sig = 0; sig < tp.split; ++sig) {
+      const float* part = a.partial + (size_t)(xcd + 8 * (tau * tp.split + sig)) * (BM * BN);
+      float4 t[QB];
+#pragma unroll
+      for (int q = 0; q < QB; ++q) t[q] = *(const float4*)(part + ((size_t)(q0 + q) * NT + tid) * 4);
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        sum[q0 + q].x += t[q].x; sum[q0 + q].y += t[q].y;
+        sum[q0 + q].z += t[q].z; sum[q0 + q].w += t[q].w;
       }
     }
   }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < NACC / 4; ++v) {
+        const float4 u = sum[(i * FN + j) * (NACC / 4) + v];
+        acc[i][j][4 * v] = u.x; acc[i][j][4 * v + 1] = u.y; acc[i][j][4 * v + 2] = u.z; acc[i][j][4 * v + 3] = u.w;
+      }
+  gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
 }
 
 // fp32 activations and weights: vector-ALU tiles (64 x 64 outputs, 4 x 4 per
@@ -521,10 +676,16 @@ static int device_cus() {
   return cached[dev];
 }
 
+// Workgroups of a persistent launch the split-K workspace is sized for; a
+// larger launch (more CUs than an MI355X) simply runs without the split.
+constexpr int kSplitGrid = 512;
+
 // Persistent launch: as many workgroups as fit on the device at once (a
-// multiple of 8, at least 8), never more than there are tiles.
+// multiple of 8, at least 8), never more than there are tiles.  With a
+// split-K workspace (a.partial) the tail tiles are split and a second
+// kernel reduces them.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF = 16>
-hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st) {
+hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial_bytes = 0) {
   auto kern = grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF>;
   constexpr int NT = 64 * WM * WN;
   a.m_tiles = (int)ceil_div(rows_cap, BM);
@@ -540,7 +701,13 @@ hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st) {
   int64_t grid = (int64_t)device_cus() * occ;
   if (grid > tiles) grid = tiles;
   grid = grid < 8 ? 8 : grid / 8 * 8;
+  a.grid = (int)grid;
+  if (a.partial != nullptr && (size_t)grid * BM * BN * sizeof(float) > partial_bytes) a.partial = nullptr;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.partial == nullptr) return e;
+  hipLaunchKernelGGL((grouped_gemm_fixup_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF>), dim3((unsigned)grid),
+                     dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -557,20 +724,33 @@ static hipError_t run_f32(GemmArgs a, int64_t rows_cap, hipStream_t st) {
 // Tile shapes per regime.  BN must divide N and BK must divide K; both are
 // multiples of 64, so the wider variants fall back when needed.
 template <bool BFP8, int EPI>
-static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hipStream_t st) {
+static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hipStream_t st, size_t pb) {
   const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0, k128 = a.K % 128 == 0;
   switch (regime) {
     case 0:
-      if (n256) return run_bf16<256, 256, 64, 4, 2, 2, BFP8, EPI, 4, 32>(a, rows_cap, st);
-      if (n128) return run_bf16<256, 128, 64, 4, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
-      return run_bf16<256, 64, 64, 4, 1, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
+      if (n256) return run_bf16<256, 256, 64, 4, 2, 2, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
+      if (n128) return run_bf16<256, 128, 64, 4, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
+      return run_bf16<256, 64, 64, 4, 1, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
     case 1:
-      if (n256) return run_bf16<128, 256, 64, 2, 4, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
-      if (n128) return run_bf16<128, 128, 64, 2, 4, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
-      return run_bf16<128, 64, 64, 2, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st);
+      if (n256) return run_bf16<128, 256, 64, 2, 4, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
+      if (n128) return run_bf16<128, 128, 64, 2, 4, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
+      return run_bf16<128, 64, 64, 2, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
     default:
-      if (k128) return run_bf16<16, 64, 128, 1, 4, 5, BFP8, EPI, 1>(a, rows_cap, st);
-      return run_bf16<16, 64, 64, 1, 2, 8, BFP8, EPI, 1>(a, rows_cap, st);  // 128 threads: A tile is 128 chunks
+      if (k128) return run_bf16<16, 64, 128, 1, 4, 5, BFP8, EPI, 1>(a, rows_cap, st, pb);
+      return run_bf16<16, 64, 64, 1, 2, 8, BFP8, EPI, 1>(a, rows_cap, st, pb);  // 128 threads: A tile is 128 chunks
+  }
+}
+
+// Bytes of split-K workspace the expert GEMMs of problem p can use (one
+// float32 tile per workgroup of a persistent launch of up to kSplitGrid).
+// The decode regime (a few rows per expert) streams weights with small
+// tiles in whole rounds; it gets no split (and no second launch).
+size_t expert_split_bytes(const Problem& p) {
+  if (p.act == DT_F32) return 0;
+  switch (gemm_regime(p)) {
+    case 0: return (size_t)kSplitGrid * 256 * 256 * sizeof(float);
+    case 1: return (size_t)kSplitGrid * 128 * 256 * sizeof(float);
+    default: return 0;
   }
 }
 
@@ -581,36 +761,41 @@ static GemmArgs expert_args(const Problem& p, const int32_t* counts, const int32
 }
 
 template <int EPI>
-static hipError_t run_expert_gemm(const Problem& p, const GemmArgs& g, int64_t rows_cap, hipStream_t st) {
+static hipError_t run_expert_gemm(const Problem& p, const GemmArgs& g, int64_t rows_cap, hipStream_t st,
+                                  size_t partial_bytes) {
   if (p.act == DT_F32) return run_f32<EPI>(g, rows_cap, st);
-  if (p.w == DT_FP8) return run_regime<true, EPI>(gemm_regime(p), g, rows_cap, st);
-  return run_regime<false, EPI>(gemm_regime(p), g, rows_cap, st);
+  if (p.w == DT_FP8) return run_regime<true, EPI>(gemm_regime(p), g, rows_cap, st, partial_bytes);
+  return run_regime<false, EPI>(gemm_regime(p), g, rows_cap, st, partial_bytes);
 }
 
 // h = GeLU(x_perm W1^T + b1) over the expert groups.
 hipError_t launch_expert_up(const Problem& p, int64_t rows_cap, const void* x_perm,
                             const int32_t* counts, const int32_t* offsets, const void* W1,
-                            const void* b1, const float* s1, void* h, hipStream_t st) {
+                            const void* b1, const float* s1, void* h, float* partial,
+                            size_t partial_bytes, hipStream_t st) {
   GemmArgs g = expert_args(p, counts, offsets);
+  g.partial = partial;
   g.A = x_perm; g.lda = p.d;
   g.B = W1; g.ldb = p.d; g.b_gstride = (int64_t)p.d_ff * p.d;
   g.scale = s1; g.bias = b1;
   g.C = h; g.ldc = p.d_ff;
   g.N = p.d_ff; g.K = p.d;
-  return run_expert_gemm<EPI_GELU>(p, g, rows_cap, st);
+  return run_expert_gemm<EPI_GELU>(p, g, rows_cap, st, partial_bytes);
 }
 
 // y_perm = h W2^T + b2 over the expert groups.
 hipError_t launch_expert_down(const Problem& p, int64_t rows_cap, const void* h,
                               const int32_t* counts, const int32_t* offsets, const void* W2,
-                              const void* b2, const float* s2, void* y_perm, hipStream_t st) {
+                              const void* b2, const float* s2, void* y_perm, float* partial,
+                              size_t partial_bytes, hipStream_t st) {
   GemmArgs g = expert_args(p, counts, offsets);
+  g.partial = partial;
   g.A = h; g.lda = p.d_ff;
   g.B = W2; g.ldb = p.d_ff; g.b_gstride = (int64_t)p.d * p.d_ff;
   g.scale = s2; g.bias = b2;
   g.C = y_perm; g.ldc = p.d;
   g.N = p.d; g.K = p.d_ff;
-  return run_expert_gemm<EPI_BIAS>(p, g, rows_cap, st);
+  return run_expert_gemm<EPI_BIAS>(p, g, rows_cap, st, partial_bytes);
 }
 
 // Router scores x W_r^T (+ router_bias) as one bf16 MFMA GEMM (E % 64 == 0).

@@ -96,8 +96,8 @@ def test_invalid_problems_rejected(kw, status):
     assert lib.moe_permute(ctypes.byref(p), *([fake] * 7), fake, 1 << 40, None) == status
     assert lib.moe_expert_ffn(ctypes.byref(p), *([fake] * 11), fake, 1 << 40, None) == status
     assert lib.moe_combine(ctypes.byref(p), *([fake] * 4), None) == status
-    assert lib.moe_expert_up(ctypes.byref(p), *([fake] * 7), None) == status
-    assert lib.moe_expert_down(ctypes.byref(p), *([fake] * 7), None) == status
+    assert lib.moe_expert_up(ctypes.byref(p), *([fake] * 7), None, 0, None) == status
+    assert lib.moe_expert_down(ctypes.byref(p), *([fake] * 7), None, 0, None) == status
 
 
 def test_null_problem_and_status_strings():
@@ -145,8 +145,8 @@ def test_empty_batch_is_a_noop_without_device():
     assert lib.moe_permute(ctypes.byref(p), *([None] * 7), None, 0, None) == M.MOE_OK
     assert lib.moe_expert_ffn(ctypes.byref(p), *([None] * 11), None, 0, None) == M.MOE_OK
     assert lib.moe_combine(ctypes.byref(p), *([None] * 4), None) == M.MOE_OK
-    assert lib.moe_expert_up(ctypes.byref(p), *([None] * 7), None) == M.MOE_OK
-    assert lib.moe_expert_down(ctypes.byref(p), *([None] * 7), None) == M.MOE_OK
+    assert lib.moe_expert_up(ctypes.byref(p), *([None] * 7), None, 0, None) == M.MOE_OK
+    assert lib.moe_expert_down(ctypes.byref(p), *([None] * 7), None, 0, None) == M.MOE_OK
 
 
 @pytest.mark.parametrize("S,E,K", [(4096, 8, 2), (16, 8, 2), (8192, 64, 4), (4096, 256, 8), (1, 8, 2), (3, 512, 64)])
