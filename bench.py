@@ -9,6 +9,8 @@ bounded sample of the same workload.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--no-decode]
+       python bench.py --pmc-probe [--workload NAME]     (under rocprofv3 --pmc)
+       python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
 """
 import argparse
 import hashlib
@@ -38,6 +40,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="only launch a 1 GiB copy and the expert GEMMs (for rocprofv3 --pmc passes)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_*.md from two rocprofv3 --pmc output directories")
     return ap.parse_args()
 
 
@@ -131,17 +137,117 @@ def gemm_source_hash():
     return h.hexdigest()[:16]
 
 
+def traffic_path(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+
+
 def traffic_for(kernel, workload):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or
     None when absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    path = traffic_path(kernel, workload)
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("source_hash") != gemm_source_hash():
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].strip().split(": ", 1)
+            vals[k.strip("`")] = v.strip().strip("`")
+    if vals.get("source_hash") != gemm_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    try:
+        return int(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+COPY_PROBE_BYTES = 1 << 30   # plain device copy of known size: scales the HBM counters
+
+
+def pmc_probe(a, D, M, torch):
+    """Launch only what the counter passes need: a plain 1 GiB device copy
+    (three times) and the workload's two expert GEMM stages (three times
+    each), so FETCH_SIZE / WRITE_SIZE per dispatch can be read off."""
+    cfg = D.CONFIGS[a.workload]
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    w = Workload(cfg, D, M, torch)
+    st = w.stages()
+    st["route"]()
+    st["permute"]()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        st["expert_up"]()
+        st["expert_down"]()
+    torch.cuda.synchronize()
+    log(f"[bench] pmc probe done: {cfg.name}")
+
+
+def pmc_summary(a):
+    """Turn the two counter passes (rocprofv3 --pmc FETCH_SIZE, then
+    WRITE_SIZE, csv output) into profiles/traffic_<stage>_<workload>.md."""
+    import csv
+    import statistics
+
+    def read(d):
+        rows = []
+        for root, _, files in os.walk(d):
+            for f in files:
+                if f.endswith("counter_collection.csv"):
+                    rows += list(csv.DictReader(open(os.path.join(root, f))))
+        return rows
+
+    fetch, write = read(a.pmc_summary[0]), read(a.pmc_summary[1])
+
+    def per_kernel(rows, counter):
+        out = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    fk, wk = per_kernel(fetch, "FETCH_SIZE"), per_kernel(write, "WRITE_SIZE")
+    # the probe's three 1 GiB copies are by far the largest copy dispatches of
+    # the run; each reads and writes COPY_PROBE_BYTES
+    ck = next(k for k in fk if "copy" in k.lower() and len(fk[k]) >= 3
+              and max(fk[k]) * 1024 > COPY_PROBE_BYTES / 4)
+    f_scale = statistics.median(sorted(fk[ck])[-3:]) * 1024 / COPY_PROBE_BYTES
+    w_scale = statistics.median(sorted(wk[ck])[-3:]) * 1024 / COPY_PROBE_BYTES
+    gemms = {k: v for k, v in fk.items() if "grouped_gemm_bf16_kernel" in k}
+    # expert_up: epilogue 0 (bias+GeLU); expert_down: epilogue 1 (bias)
+    stages = {}
+    for k in gemms:
+        args = k.split("<", 1)[1].split(">", 1)[0].split(",")
+        stages["expert_up" if args[7].strip() == "0" else "expert_down"] = k
+    cfg_name = a.workload
+    for stage, k in stages.items():
+        fb = statistics.median(fk[k]) * 1024 / f_scale
+        wb = statistics.median(wk[k]) * 1024 / w_scale
+        path = traffic_path(stage, cfg_name)
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic: `{stage}` GEMM, {cfg_name} workload\n\n")
+            f.write("Commands (one MI355X, repository root; two counter passes, then this summary):\n\n```\n")
+            f.write(f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o f --output-format csv -- "
+                    f"python -u bench.py --pmc-probe --workload {cfg_name}\n")
+            f.write(f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o w --output-format csv -- "
+                    f"python -u bench.py --pmc-probe --workload {cfg_name}\n")
+            f.write(f"python bench.py --workload {cfg_name} --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write\n```\n\n")
+            f.write(f"Kernel: `{k}` ({len(fk[k])} dispatches, median per dispatch).\n\n")
+            f.write("| counter | raw (KiB per dispatch) | plain-copy scale (counter bytes / true bytes) | HBM bytes per launch |\n")
+            f.write("|:--|--:|--:|--:|\n")
+            f.write(f"| FETCH_SIZE | {statistics.median(fk[k]):.0f} | {f_scale:.4f} | {fb:.4g} |\n")
+            f.write(f"| WRITE_SIZE | {statistics.median(wk[k]):.0f} | {w_scale:.4f} | {wb:.4g} |\n\n")
+            f.write(f"The scale comes from a plain {COPY_PROBE_BYTES >> 20} MiB device copy in the same run "
+                    f"(`{ck[:60]}`), which reads and writes exactly that many bytes.\n\n")
+            f.write(f"- bytes_per_launch: {int(round(fb + wb))}\n")
+            f.write(f"- fetch_bytes: {int(round(fb))}\n")
+            f.write(f"- write_bytes: {int(round(wb))}\n")
+            f.write(f"- source_hash: {gemm_source_hash()}\n")
+        log(f"[bench] wrote {path}")
 
 
 def roofline(cfg, stage_ms, touched, workload):
@@ -220,6 +326,9 @@ def cpu_baseline(cfg, w, target_s, torch):
 
 def main():
     a = parse()
+    if a.pmc_summary:
+        pmc_summary(a)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(json.dumps({"metric": METRIC, "error": "this build runs on exactly one GPU; "
@@ -233,6 +342,9 @@ def main():
     M.lib()   # raises if the HIP library is missing: there is no fallback
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if a.pmc_probe:
+        pmc_probe(a, D, M, torch)
+        return
     cfg, w, ms, stage_ms, touched, counts = run_workload(a.workload, a.steps, a.warmup, D, M, torch)
     mean = cfg.S * cfg.K / cfg.E
     out = {
