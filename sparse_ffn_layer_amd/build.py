@@ -54,7 +54,7 @@ def _check_no_scratch(src: str, remarks: str) -> None:
             name = m.group(1)
             continue
         m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
-        if m and name and "grouped_gemm_bf16_kernel" in name and int(m.group(1)) > 0:
+        if m and name and "grouped_gemm_bf16" in name and int(m.group(1)) > 0:
             raise RuntimeError(f"{src}: kernel {name} spills ({m.group(1)} scratch bytes/lane)")
 
 

@@ -133,4 +133,12 @@ __device__ __forceinline__ void buffer_load_lds_16(i32x4_t rsrc, void* lds_base,
   llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_void_t*)lds_base, 16, (int)voffset, (int)soffset, 0, 0);
 }
 
+// 16-byte global -> VGPR load through a buffer resource (range-checked:
+// bytes past num_records read as zero, with no memory access).
+__device__ i32x4_t llvm_amdgcn_raw_buffer_load_v4i32(i32x4_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ __forceinline__ i32x4_t buffer_load_16(i32x4_t rsrc, uint32_t voffset, uint32_t soffset) {
+  return llvm_amdgcn_raw_buffer_load_v4i32(rsrc, (int)voffset, (int)soffset, 0);
+}
+
 }  // namespace sfl

@@ -155,11 +155,29 @@ __device__ __forceinline__ bool tile_coords(const GemmArgs& a, int m_used, int64
 // Epilogue of one tile: lane holds out[m][n .. n+3] for m = lane % MF and,
 // per group q4 of four accumulators, n = (MF == 16 ? 4 * lk : 8 * q4 + 4 * lk);
 // scale (fp8), bias, optional exact GeLU, round, store the valid rows.
-template <int BN, int WM, int WN, bool BFP8, int EPI, int MF, int FM, int FN, int NACC, typename acc_t>
+// Accumulator element k.  AREAD: the accumulators live in AGPRs and are read
+// one element at a time with v_accvgpr_read where they are used; otherwise
+// the register allocator may copy all of them to VGPRs at once.
+template <bool AREAD, typename acc_t>
+__device__ __forceinline__ float acc_get(const acc_t& v, int k) {
+  if constexpr (AREAD) {
+    float f;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(f) : "a"(v[k]));
+    return f;
+  } else {
+    return v[k];
+  }
+}
+
+template <int BN, int WM, int WN, bool BFP8, int EPI, int MF, int FM, int FN, int NACC, bool AREAD = false,
+          typename acc_t>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const acc_t (&acc)[FM][FN], int g, int rows,
                                               int64_t row0, int n0, int wm, int wn, int lr, int lk) {
   constexpr int WTN = BN / WN;
   const int WTM = FM * MF;
+  // the lane's output addresses are computed here, not hoisted before the
+  // main loop (where they would stay live through it)
+  asm volatile("" : "+v"(lr), "+v"(lk));
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -191,7 +209,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const acc_t (&a
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            float t = BFP8 ? acc[i][j][q4 * 4 + q] * sc[q] : acc[i][j][q4 * 4 + q];
+            const float x = acc_get<AREAD>(acc[i][j], q4 * 4 + q);
+            float t = BFP8 ? x * sc[q] : x;
             t += bi[q];
             if constexpr (EPI == EPI_GELU) t = gelu_erf(t);
             v[q] = t;
@@ -585,6 +604,203 @@ grouped_gemm_fixup_kernel(const GemmArgs a) {
   gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
 }
 
+// bf16 prefill tiles of 256 x 256 with four waves (one per SIMD), each wave
+// owning a 128 x 128 quarter: 16 accumulator blocks of 32 x 32 in AGPRs (all
+// 256), so every 16-byte fragment read from LDS feeds four MFMAs.  The tile's
+// global loads are staged in VGPRs: stage kt + 2 is loaded during stage kt
+// and written to LDS during stage kt + 1, into the slot that the barrier
+// ending stage kt freed.  Every k-step interleaves its LDS reads, LDS writes
+// and global loads one or two per MFMA; the loads of a stage are spread over
+// three k-steps, since a burst of them stalls in-order issue behind the
+// vector-memory queue and with one wave per SIMD nothing else fills the MFMA
+// pipe meanwhile.  Rows of a partly filled tile do all MFMAs (their loads
+// read zeros); only the stores skip them.
+template <int EPI>
+__global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const GemmArgs a) {
+  constexpr int BM = 256, BN = 256, BK = 64, NT = 256, GM = 4, MF = 32;
+  constexpr int CA = BK * 2 / 16;  // 16-byte chunks per row
+  constexpr int A_BYTES = BM * BK * 2, STAGE_BYTES = A_BYTES + BN * BK * 2;
+  constexpr int A_LOADS = BM * CA / NT, B_LOADS = BN * CA / NT, LOADS = A_LOADS + B_LOADS;
+  constexpr int FM = 4, FN = 4, NACC = 16, KS = BK / 16, KC = 2, NMF = FM * FN;
+  static_assert(LOADS == 16 && NMF == 16, "the k-step schedule below assumes 16 loads and 16 MFMAs");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lk = lane >> 5;
+
+  const int m_used = rows_tiles_used<BM>(a);
+  const int64_t T = (int64_t)m_used * a.n_tiles;
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;
+  const int nx = (nwg - xcd + 7) >> 3;
+  const int KT_ALL = a.K / BK;
+  const TailPlan tp = tail_plan(T, xcd, nx, a.partial != nullptr && KT_ALL >= 16);
+
+  auto run_tile = [&](int64_t L, int kt0, int kt1, float* part) {
+    int64_t row0;
+    int n0, g, rows;
+    if (!tile_coords<BM, BN, GM>(a, m_used, L, row0, n0, g, rows)) return;
+    // same resources, offsets and XOR-swizzled LDS layout as the kernel above
+    const i32x4_t rsrc_a = make_rsrc((const char*)a.A + row0 * a.lda * 2, (uint32_t)((int64_t)rows * a.lda * 2));
+    const i32x4_t rsrc_b = make_rsrc((const char*)a.B + (int64_t)g * a.b_gstride * 2 + (int64_t)n0 * a.ldb * 2,
+                                     (uint32_t)((int64_t)BN * a.ldb * 2));
+    uint32_t a_off[A_LOADS], b_off[B_LOADS];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int q = i * NT + tid, r = q / CA, s = q % CA;
+      a_off[i] = (uint32_t)(r * a.lda * 2 + (s ^ swz<CA>(r)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int q = i * NT + tid, r = q / CA, s = q % CA;
+      b_off[i] = (uint32_t)(r * a.ldb * 2 + (s ^ swz<CA>(r)) * 16);
+    }
+    i32x4_t R[LOADS];  // one stage of the tile (this thread's 16 chunks)
+    auto gload = [&](int kt, int l) {
+      const uint32_t ko = (uint32_t)((kt0 + kt) * BK * 2);
+      R[l] = l < A_LOADS ? buffer_load_16(rsrc_a, a_off[l], ko) : buffer_load_16(rsrc_b, b_off[l - A_LOADS], ko);
+    };
+    auto swrite = [&](int slot, int l) {
+      char* base = smem + slot * STAGE_BYTES + (l < A_LOADS ? 0 : A_BYTES);
+      const int ll = l < A_LOADS ? l : l - A_LOADS;
+      *(i32x4_t*)(base + (ll * NT + tid) * 16) = R[l];
+    };
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    uint32_t a_rd[FM], b_rd[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * 128 + i * MF + lr;
+      a_rd[i] = lds0 + (uint32_t)(r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * 128 + j * MF + lr;
+      b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
+    }
+    // fragment q of k-step ks (q < FM: A fragment q, else B fragment q - FM)
+    auto read_one = [&](int slot, int ks, int q, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
+      const uint32_t so = (uint32_t)(slot * STAGE_BYTES), kx = (uint32_t)((KC * ks) << 4);
+      if (q < FM) asm volatile("ds_read_b128 %0, %1" : "=v"(af[q]) : "v"((a_rd[q] ^ kx) + so));
+      else asm volatile("ds_read_b128 %0, %1" : "=v"(bf[q - FM]) : "v"((b_rd[q - FM] ^ kx) + so));
+    };
+
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < NACC; ++v) acc[i][j][v] = 0.f;
+    // wait states between the VALU writes of the zeroed AGPRs and the first
+    // MFMA reading them as its C operand
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 4" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int KT = kt1 - kt0;
+    __syncthreads();  // every wave is done with the previous tile's LDS
+    // prologue: stage 0 to slot 0, stage 1 into the registers
+#pragma unroll
+    for (int l = 0; l < LOADS; ++l) gload(0, l);
+#pragma unroll
+    for (int l = 0; l < LOADS; ++l) swrite(0, l);
+    if (KT > 1) {
+#pragma unroll
+      for (int l = 0; l < LOADS; ++l) gload(1, l);
+    }
+    barrier_lds();
+    bf16x8_t fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int q = 0; q < FM + FN; ++q) read_one(0, 0, q, fa[0], fb[0]);
+
+    // W: the registers hold stage kt + 1, to be written to slot s ^ 1; Lq:
+    // afterwards they are loaded with stage kt + 2.  Both are compile-time,
+    // so the k-steps carry no branches.
+    auto stage = [&](int kt, auto w_tag, auto l_tag) {
+      constexpr bool W = decltype(w_tag)::value, Lq = decltype(l_tag)::value;
+      const int s = kt & 1;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        wait_lgkmcnt<0>();  // this k-step's fragments and the earlier LDS writes have landed
+        if (ks == KS - 1 && W) barrier_lds();  // stage kt + 1 is visible; slot s is free
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NMF; ++t) {
+          const int i = t / FN, j = t % FN;
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fb[cur][j]), "v"(fa[cur][i]));
+          __builtin_amdgcn_sched_barrier(0);
+          // the next k-step's fragments, one read after each of the first 8 MFMAs
+          if (t < FM + FN) {
+            if (ks + 1 < KS) read_one(s, ks + 1, t, fa[nxt], fb[nxt]);
+            else if (W) read_one(s ^ 1, 0, t, fa[nxt], fb[nxt]);
+          }
+          // writes of the staged stage kt + 1: registers 0-7 in k-step 0,
+          // 8-15 in k-step 1; a register is reloaded (stage kt + 2) after its
+          // write: 0-5 in k-step 1, 6-10 in k-step 2, 11-15 in k-step 3
+          if (W && ks < 2 && (t & 1) == 0) swrite(s ^ 1, ks * 8 + t / 2);
+          if (Lq && ks == 1 && (t & 1) == 1 && t / 2 < 6) gload(kt + 2, t / 2);
+          if (Lq && ks == 2 && t % 3 == 0 && t / 3 < 5) gload(kt + 2, 6 + t / 3);
+          if (Lq && ks == 3 && t % 3 == 0 && t / 3 < 5) gload(kt + 2, 11 + t / 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    using T1 = std::integral_constant<bool, true>;
+    using T0 = std::integral_constant<bool, false>;
+    int kt = 0;
+    for (; kt + 2 < KT; ++kt) stage(kt, T1{}, T1{});
+    if (kt + 1 < KT) {
+      stage(kt, T1{}, T0{});
+      ++kt;
+    }
+    stage(kt, T0{}, T0{});
+
+    // the last MFMAs wrote the accumulators behind the compiler's back: wait
+    // out the MFMA-write -> AGPR-read hazard
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (part != nullptr) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < NACC; v += 4) {
+            const int q = ((i * FN + j) * NACC + v) / 4;
+            *(float4*)(part + ((size_t)q * NT + tid) * 4) =
+                make_float4(acc_get<true>(acc[i][j], v), acc_get<true>(acc[i][j], v + 1),
+                            acc_get<true>(acc[i][j], v + 2), acc_get<true>(acc[i][j], v + 3));
+          }
+      return;
+    }
+    gemm_epilogue<BN, 2, 2, false, EPI, MF, FM, FN, NACC, true>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
+  };
+
+  // whole tiles of the full rounds, then (with a split) this workgroup's
+  // slice of a tail tile; one call site keeps the tile body inlined once
+  const int64_t loop_end = tp.split ? tp.full_end : tp.t_hi;
+  const bool has_slice = tp.split && xj < tp.tail * tp.split;
+  for (int64_t L = tp.t_lo + xj;; L += nx) {
+    int kt0 = 0, kt1 = KT_ALL;
+    float* part = nullptr;
+    int64_t Lt = L;
+    if (L >= loop_end) {
+      if (!has_slice || L - nx >= loop_end) break;
+      const int tau = xj / tp.split, sig = xj % tp.split;
+      Lt = tp.full_end + tau;
+      kt0 = KT_ALL * sig / tp.split;
+      kt1 = KT_ALL * (sig + 1) / tp.split;
+      part = a.partial + (size_t)blockIdx.x * (BM * BN);
+    }
+    run_tile(Lt, kt0, kt1, part);
+  }
+}
+
 // fp32 activations and weights: vector-ALU tiles (64 x 64 outputs, 4 x 4 per
 // thread), exact fp32 fused multiply-adds.
 template <int EPI>
@@ -711,6 +927,28 @@ hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial
   return hipGetLastError();
 }
 
+// The four-wave 256 x 256 kernel: one workgroup per CU (it holds all 512
+// registers of each SIMD's one wave), split-K tail as above.
+template <int EPI>
+hipError_t run_bf16_w4(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial_bytes) {
+  a.m_tiles = (int)ceil_div(rows_cap, 256);
+  a.n_tiles = a.N / 256;
+  const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
+  if (tiles == 0) return hipSuccess;
+  int64_t grid = (int64_t)device_cus();
+  if (grid > tiles) grid = tiles;
+  grid = grid < 8 ? 8 : grid / 8 * 8;
+  a.grid = (int)grid;
+  if (a.partial != nullptr && (size_t)grid * 256 * 256 * sizeof(float) > partial_bytes) a.partial = nullptr;
+  hipLaunchKernelGGL(grouped_gemm_bf16_w4_kernel<EPI>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.partial == nullptr) return e;
+  // the fixup's thread layout matches: 2 x 2 waves of 128 x 128, 32 x 32 MFMAs
+  hipLaunchKernelGGL((grouped_gemm_fixup_kernel<256, 256, 64, 2, 2, 2, false, EPI, 4, 32>), dim3((unsigned)grid),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int EPI>
 static hipError_t run_f32(GemmArgs a, int64_t rows_cap, hipStream_t st) {
   a.m_tiles = (int)ceil_div(rows_cap, 64);
@@ -728,6 +966,7 @@ static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hi
   const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0, k128 = a.K % 128 == 0;
   switch (regime) {
     case 0:
+      if (!BFP8 && n256 && a.K % 64 == 0) return run_bf16_w4<EPI>(a, rows_cap, st, pb);
       if (n256) return run_bf16<256, 256, 64, 4, 2, 2, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
       if (n128) return run_bf16<256, 128, 64, 4, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
       return run_bf16<256, 64, 64, 4, 1, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
