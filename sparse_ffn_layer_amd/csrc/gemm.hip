@@ -604,17 +604,75 @@ grouped_gemm_fixup_kernel(const GemmArgs a) {
   gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
 }
 
+// Epilogue of the four-wave kernel, through LDS: bias (+ GeLU) and bf16
+// rounding in the MFMA layout, into a per-wave 128 x 128 tile in LDS (16-byte
+// chunk c of row r at slot c ^ (r & 15)), then stored by whole 256-byte row
+// segments (16 lanes per row, 4 rows per store instruction) instead of 16-byte
+// pieces of 32 rows.  The bias of all the lane's channels is loaded first so
+// the loads overlap.  The caller has made every wave finish with the k-stages
+// in LDS.
+template <int EPI>
+__device__ __forceinline__ void w4_epilogue(const GemmArgs& a, const f32x16_t (&acc)[4][4], int g, int rows,
+                                            int64_t row0, int n0, int wm, int wn, int lr, int lk, int lane, char* wt) {
+  asm volatile("" : "+v"(lr), "+v"(lk));  // addresses computed here, not hoisted into the main loop
+  uint2 bias[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int n = n0 + wn * 128 + j * 32 + q4 * 8 + lk * 4;
+      bias[j][q4] = a.bias != nullptr ? *(const uint2*)((const uint16_t*)a.bias + (int64_t)g * a.N + n) : make_uint2(0, 0);
+    }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // one group of accumulators at a time (read from AGPRs where used)
+      __builtin_amdgcn_sched_barrier(0);
+      const uint2 b2 = bias[j][q4];
+      const float bi[4] = {bf16_bits_to_f32(b2.x & 0xffff), bf16_bits_to_f32(b2.x >> 16),
+                           bf16_bits_to_f32(b2.y & 0xffff), bf16_bits_to_f32(b2.y >> 16)};
+      const int cc = j * 4 + q4;  // 16-byte chunk of the wave tile's row: channels 8 cc .. 8 cc + 7
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (wm * 128 + i * 32 >= rows) continue;  // uniform: fragment wholly past the rows
+        const int r = i * 32 + lr;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float t = acc_get<true>(acc[i][j], q4 * 4 + q) + bi[q];
+          if constexpr (EPI == EPI_GELU) t = gelu_erf(t);
+          v[q] = t;
+        }
+        *(uint2*)(wt + r * 256 + ((cc ^ (r & 15)) << 4) + lk * 8) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+  wait_lgkmcnt<0>();  // the wave reads back only its own tile
+  const int c = lane & 15;
+#pragma unroll 4
+  for (int rr = 0; rr < 128; rr += 4) {
+    const int r = rr + (lane >> 4);
+    const uint4 val = *(const uint4*)(wt + r * 256 + ((c ^ (r & 15)) << 4));
+    const int m = wm * 128 + r;
+    if (m < rows) *(uint4*)((uint16_t*)a.C + (row0 + m) * a.ldc + n0 + wn * 128 + c * 8) = val;
+  }
+}
+
 // bf16 prefill tiles of 256 x 256 with four waves (one per SIMD), each wave
 // owning a 128 x 128 quarter: 16 accumulator blocks of 32 x 32 in AGPRs (all
-// 256), so every 16-byte fragment read from LDS feeds four MFMAs.  The tile's
-// global loads are staged in VGPRs: stage kt + 2 is loaded during stage kt
-// and written to LDS during stage kt + 1, into the slot that the barrier
-// ending stage kt freed.  Every k-step interleaves its LDS reads, LDS writes
-// and global loads one or two per MFMA; the loads of a stage are spread over
-// three k-steps, since a burst of them stalls in-order issue behind the
-// vector-memory queue and with one wave per SIMD nothing else fills the MFMA
-// pipe meanwhile.  Rows of a partly filled tile do all MFMAs (their loads
-// read zeros); only the stores skip them.
+// 256), so every 16-byte fragment read from LDS feeds four MFMAs.
+//
+// The tile's global loads are staged in VGPRs: stage kt + 2 is loaded during
+// stage kt and written to LDS during stage kt + 1, into the slot that the
+// barrier ending stage kt freed.  Every k-step interleaves its LDS reads, LDS
+// writes and global loads one or two per MFMA; the loads of a stage are
+// spread over three k-steps, since a burst of them stalls in-order issue
+// behind the vector-memory queue and with one wave per SIMD nothing else
+// fills the MFMA pipe meanwhile.  The last stage of a tile loads the next
+// tile's first stage the same way, so those loads fly during the epilogue.
+// Rows of a partly filled tile do all MFMAs (their loads read zeros); only
+// the stores skip them.
 template <int EPI>
 __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const GemmArgs a) {
   constexpr int BM = 256, BN = 256, BK = 64, NT = 256, GM = 4, MF = 32;
@@ -623,6 +681,7 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
   constexpr int A_LOADS = BM * CA / NT, B_LOADS = BN * CA / NT, LOADS = A_LOADS + B_LOADS;
   constexpr int FM = 4, FN = 4, NACC = 16, KS = BK / 16, KC = 2, NMF = FM * FN;
   static_assert(LOADS == 16 && NMF == 16, "the k-step schedule below assumes 16 loads and 16 MFMAs");
+  static_assert(2 * STAGE_BYTES >= 4 * 128 * 256, "the epilogue's per-wave tiles fit in the stage buffers");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
 
   const int tid = threadIdx.x;
@@ -639,54 +698,93 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
   const int KT_ALL = a.K / BK;
   const TailPlan tp = tail_plan(T, xcd, nx, a.partial != nullptr && KT_ALL >= 16);
 
-  auto run_tile = [&](int64_t L, int kt0, int kt1, float* part) {
+  // Work item k of this workgroup: whole tiles of the full rounds, then
+  // (with a split) one k-slice of a tail tile.
+  struct Item {
     int64_t row0;
-    int n0, g, rows;
-    if (!tile_coords<BM, BN, GM>(a, m_used, L, row0, n0, g, rows)) return;
-    // same resources, offsets and XOR-swizzled LDS layout as the kernel above
-    const i32x4_t rsrc_a = make_rsrc((const char*)a.A + row0 * a.lda * 2, (uint32_t)((int64_t)rows * a.lda * 2));
-    const i32x4_t rsrc_b = make_rsrc((const char*)a.B + (int64_t)g * a.b_gstride * 2 + (int64_t)n0 * a.ldb * 2,
-                                     (uint32_t)((int64_t)BN * a.ldb * 2));
-    uint32_t a_off[A_LOADS], b_off[B_LOADS];
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int q = i * NT + tid, r = q / CA, s = q % CA;
-      a_off[i] = (uint32_t)(r * a.lda * 2 + (s ^ swz<CA>(r)) * 16);
+    int n0, g, rows, kt0, kt1;
+    float* part;
+    i32x4_t ra, rb;  // buffer resources of the tile's A rows and B rows
+  };
+  const int64_t loop_end = tp.split ? tp.full_end : tp.t_hi;
+  const bool has_slice = tp.split && xj < tp.tail * tp.split;
+  // the first valid item at index >= k (k is advanced past it)
+  auto next_item = [&](int& k, Item& it) -> bool {
+    for (;; ++k) {
+      const int64_t L = tp.t_lo + xj + (int64_t)k * nx;
+      int64_t Lt = L;
+      it.kt0 = 0;
+      it.kt1 = KT_ALL;
+      it.part = nullptr;
+      if (L >= loop_end) {
+        if (!has_slice || L - nx >= loop_end) return false;  // the slice comes once, after the whole tiles
+        const int tau = xj / tp.split, sig = xj % tp.split;
+        Lt = tp.full_end + tau;
+        it.kt0 = KT_ALL * sig / tp.split;
+        it.kt1 = KT_ALL * (sig + 1) / tp.split;
+        it.part = a.partial + (size_t)blockIdx.x * (BM * BN);
+      }
+      if (!tile_coords<BM, BN, GM>(a, m_used, Lt, it.row0, it.n0, it.g, it.rows)) continue;
+      // exact ranges: chunks of rows past the group's count are dropped (zeros,
+      // no access).  The values are wave-uniform; readfirstlane says so, so
+      // the resources stay in SGPRs (a buffer load needs them there).
+      auto uni = [](i32x4_t v) {
+        return i32x4_t{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                       __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w)};
+      };
+      it.ra = uni(make_rsrc((const char*)a.A + it.row0 * a.lda * 2, (uint32_t)((int64_t)it.rows * a.lda * 2)));
+      it.rb = uni(make_rsrc((const char*)a.B + (int64_t)it.g * a.b_gstride * 2 + (int64_t)it.n0 * a.ldb * 2,
+                            (uint32_t)((int64_t)BN * a.ldb * 2)));
+      ++k;
+      return true;
     }
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const int q = i * NT + tid, r = q / CA, s = q % CA;
-      b_off[i] = (uint32_t)(r * a.ldb * 2 + (s ^ swz<CA>(r)) * 16);
-    }
-    i32x4_t R[LOADS];  // one stage of the tile (this thread's 16 chunks)
-    auto gload = [&](int kt, int l) {
-      const uint32_t ko = (uint32_t)((kt0 + kt) * BK * 2);
-      R[l] = l < A_LOADS ? buffer_load_16(rsrc_a, a_off[l], ko) : buffer_load_16(rsrc_b, b_off[l - A_LOADS], ko);
-    };
-    auto swrite = [&](int slot, int l) {
-      char* base = smem + slot * STAGE_BYTES + (l < A_LOADS ? 0 : A_BYTES);
-      const int ll = l < A_LOADS ? l : l - A_LOADS;
-      *(i32x4_t*)(base + (ll * NT + tid) * 16) = R[l];
-    };
-    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-    uint32_t a_rd[FM], b_rd[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = wm * 128 + i * MF + lr;
-      a_rd[i] = lds0 + (uint32_t)(r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = wn * 128 + j * MF + lr;
-      b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
-    }
-    // fragment q of k-step ks (q < FM: A fragment q, else B fragment q - FM)
-    auto read_one = [&](int slot, int ks, int q, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
-      const uint32_t so = (uint32_t)(slot * STAGE_BYTES), kx = (uint32_t)((KC * ks) << 4);
-      if (q < FM) asm volatile("ds_read_b128 %0, %1" : "=v"(af[q]) : "v"((a_rd[q] ^ kx) + so));
-      else asm volatile("ds_read_b128 %0, %1" : "=v"(bf[q - FM]) : "v"((b_rd[q - FM] ^ kx) + so));
-    };
+  };
 
+  // per-thread chunk offsets (the same for every tile); same XOR-swizzled
+  // LDS layout as the kernel above
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int q = i * NT + tid, r = q / CA, s = q % CA;
+    a_off[i] = (uint32_t)(r * a.lda * 2 + (s ^ swz<CA>(r)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int q = i * NT + tid, r = q / CA, s = q % CA;
+    b_off[i] = (uint32_t)(r * a.ldb * 2 + (s ^ swz<CA>(r)) * 16);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  uint32_t a_rd[FM], b_rd[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * 128 + i * MF + lr;
+    a_rd[i] = lds0 + (uint32_t)(r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int r = wn * 128 + j * MF + lr;
+    b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
+  }
+  i32x4_t R[LOADS];  // one stage of a tile (this thread's 16 chunks)
+  auto gload = [&](const Item& it, int kt, int l) {
+    const uint32_t ko = (uint32_t)((it.kt0 + kt) * BK * 2);
+    R[l] = l < A_LOADS ? buffer_load_16(it.ra, a_off[l], ko) : buffer_load_16(it.rb, b_off[l - A_LOADS], ko);
+  };
+  auto swrite = [&](int slot, int l) {
+    char* base = smem + slot * STAGE_BYTES + (l < A_LOADS ? 0 : A_BYTES);
+    const int ll = l < A_LOADS ? l : l - A_LOADS;
+    *(i32x4_t*)(base + (ll * NT + tid) * 16) = R[l];
+  };
+  // fragment q of k-step ks (q < FM: A fragment q, else B fragment q - FM)
+  auto read_one = [&](int slot, int ks, int q, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
+    const uint32_t so = (uint32_t)(slot * STAGE_BYTES), kx = (uint32_t)((KC * ks) << 4);
+    if (q < FM) asm volatile("ds_read_b128 %0, %1" : "=v"(af[q]) : "v"((a_rd[q] ^ kx) + so));
+    else asm volatile("ds_read_b128 %0, %1" : "=v"(bf[q - FM]) : "v"((b_rd[q - FM] ^ kx) + so));
+  };
+
+  // one tile; pre: its stage 0 is already in R; has_next: the last stage
+  // loads stage 0 of `nit` (the next item) into R
+  auto run_tile = [&](const Item& it, bool pre, bool has_next, const Item& nit) {
     f32x16_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -700,16 +798,18 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
     asm volatile("s_nop 4" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
-    const int KT = kt1 - kt0;
+    const int KT = it.kt1 - it.kt0;
     __syncthreads();  // every wave is done with the previous tile's LDS
     // prologue: stage 0 to slot 0, stage 1 into the registers
+    if (!pre) {
 #pragma unroll
-    for (int l = 0; l < LOADS; ++l) gload(0, l);
+      for (int l = 0; l < LOADS; ++l) gload(it, 0, l);
+    }
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) swrite(0, l);
     if (KT > 1) {
 #pragma unroll
-      for (int l = 0; l < LOADS; ++l) gload(1, l);
+      for (int l = 0; l < LOADS; ++l) gload(it, 1, l);
     }
     barrier_lds();
     bf16x8_t fa[2][FM], fb[2][FN];
@@ -717,10 +817,12 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
     for (int q = 0; q < FM + FN; ++q) read_one(0, 0, q, fa[0], fb[0]);
 
     // W: the registers hold stage kt + 1, to be written to slot s ^ 1; Lq:
-    // afterwards they are loaded with stage kt + 2.  Both are compile-time,
-    // so the k-steps carry no branches.
+    // afterwards they are loaded with stage kt + 2; P (last stage): they are
+    // loaded with the next tile's stage 0.  W and Lq are compile-time, so the
+    // k-steps carry no branches.
     auto stage = [&](int kt, auto w_tag, auto l_tag) {
       constexpr bool W = decltype(w_tag)::value, Lq = decltype(l_tag)::value;
+      constexpr bool LAST = !W && !Lq;
       const int s = kt & 1;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -739,12 +841,19 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
             else if (W) read_one(s ^ 1, 0, t, fa[nxt], fb[nxt]);
           }
           // writes of the staged stage kt + 1: registers 0-7 in k-step 0,
-          // 8-15 in k-step 1; a register is reloaded (stage kt + 2) after its
-          // write: 0-5 in k-step 1, 6-10 in k-step 2, 11-15 in k-step 3
+          // 8-15 in k-step 1; a register is reloaded after its write: 0-5 in
+          // k-step 1, 6-10 in k-step 2, 11-15 in k-step 3
           if (W && ks < 2 && (t & 1) == 0) swrite(s ^ 1, ks * 8 + t / 2);
-          if (Lq && ks == 1 && (t & 1) == 1 && t / 2 < 6) gload(kt + 2, t / 2);
-          if (Lq && ks == 2 && t % 3 == 0 && t / 3 < 5) gload(kt + 2, 6 + t / 3);
-          if (Lq && ks == 3 && t % 3 == 0 && t / 3 < 5) gload(kt + 2, 11 + t / 3);
+          int l = -1;
+          if (ks == 1 && (t & 1) == 1 && t / 2 < 6) l = t / 2;
+          if (ks == 2 && t % 3 == 0 && t / 3 < 5) l = 6 + t / 3;
+          if (ks == 3 && t % 3 == 0 && t / 3 < 5) l = 11 + t / 3;
+          if (l >= 0) {
+            if constexpr (Lq) gload(it, kt + 2, l);
+            if constexpr (LAST) {
+              if (has_next) gload(nit, 0, l);
+            }
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -764,7 +873,9 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    if (part != nullptr) {
+    if (it.part != nullptr) {
+      // split-K slice: raw accumulators in 16-byte groups, group-major so
+      // consecutive threads store consecutive 16 bytes
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -772,32 +883,25 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
 #pragma unroll
           for (int v = 0; v < NACC; v += 4) {
             const int q = ((i * FN + j) * NACC + v) / 4;
-            *(float4*)(part + ((size_t)q * NT + tid) * 4) =
+            *(float4*)(it.part + ((size_t)q * NT + tid) * 4) =
                 make_float4(acc_get<true>(acc[i][j], v), acc_get<true>(acc[i][j], v + 1),
                             acc_get<true>(acc[i][j], v + 2), acc_get<true>(acc[i][j], v + 3));
           }
       return;
     }
-    gemm_epilogue<BN, 2, 2, false, EPI, MF, FM, FN, NACC, true>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
+    __syncthreads();  // every wave is done reading the k-stages in LDS
+    w4_epilogue<EPI>(a, acc, it.g, it.rows, it.row0, it.n0, wm, wn, lr, lk, lane, smem + wave * (128 * 256));
   };
 
-  // whole tiles of the full rounds, then (with a split) this workgroup's
-  // slice of a tail tile; one call site keeps the tile body inlined once
-  const int64_t loop_end = tp.split ? tp.full_end : tp.t_hi;
-  const bool has_slice = tp.split && xj < tp.tail * tp.split;
-  for (int64_t L = tp.t_lo + xj;; L += nx) {
-    int kt0 = 0, kt1 = KT_ALL;
-    float* part = nullptr;
-    int64_t Lt = L;
-    if (L >= loop_end) {
-      if (!has_slice || L - nx >= loop_end) break;
-      const int tau = xj / tp.split, sig = xj % tp.split;
-      Lt = tp.full_end + tau;
-      kt0 = KT_ALL * sig / tp.split;
-      kt1 = KT_ALL * (sig + 1) / tp.split;
-      part = a.partial + (size_t)blockIdx.x * (BM * BN);
-    }
-    run_tile(Lt, kt0, kt1, part);
+  int k = 0;
+  Item cur, nit;
+  bool have = next_item(k, cur), pre = false;
+  while (have) {
+    const bool has_next = next_item(k, nit);
+    run_tile(cur, pre, has_next, nit);  // one call site keeps the tile body inlined once
+    pre = has_next;
+    cur = nit;
+    have = has_next;
   }
 }
 
