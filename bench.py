@@ -217,12 +217,16 @@ def pmc_summary(a):
               and max(fk[k]) * 1024 > COPY_PROBE_BYTES / 4)
     f_scale = statistics.median(sorted(fk[ck])[-3:]) * 1024 / COPY_PROBE_BYTES
     w_scale = statistics.median(sorted(wk[ck])[-3:]) * 1024 / COPY_PROBE_BYTES
-    gemms = {k: v for k, v in fk.items() if "grouped_gemm_bf16_kernel" in k}
-    # expert_up: epilogue 0 (bias+GeLU); expert_down: epilogue 1 (bias)
+    # the expert GEMM kernels: expert_up has epilogue 0 (bias+GeLU), expert_down
+    # epilogue 1 (bias); the epilogue is the only template argument of the
+    # four-wave kernel and the eighth of the general one
     stages = {}
-    for k in gemms:
-        args = k.split("<", 1)[1].split(">", 1)[0].split(",")
-        stages["expert_up" if args[7].strip() == "0" else "expert_down"] = k
+    for k in fk:
+        if "grouped_gemm_bf16" not in k or "fixup" in k:
+            continue
+        args = [x.strip() for x in k.split("<", 1)[1].split(">", 1)[0].split(",")]
+        epi = args[0] if "_w4_kernel" in k else args[7]
+        stages["expert_up" if epi == "0" else "expert_down"] = k
     cfg_name = a.workload
     for stage, k in stages.items():
         fb = statistics.median(fk[k]) * 1024 / f_scale
