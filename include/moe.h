@@ -81,6 +81,12 @@ typedef enum {
  *    K <= topk_groups * E / n_groups.
  *  - renormalize: 1 = gates are the softmax over the K chosen scores (sum to
  *    1); 0 = gates are the chosen experts' full-softmax probabilities.
+ *  - gate_temperature: the gates are computed from score / tau (chapter 11
+ *    section 11.3.3, soft routing: a higher tau spreads the weights more
+ *    evenly; with K = E this is the soft-routing layer).  Selection does not
+ *    depend on it.  0 means 1 (so a zero-initialised problem keeps plain
+ *    gates); tau must otherwise be positive and finite, else
+ *    MOE_ERR_INVALID_ARG.
  *  - Limits: 1 <= E <= 512, 1 <= K <= min(E, 64), d and d_ff multiples of 64,
  *    S < 2^31 / K.  Outside them: MOE_ERR_UNSUPPORTED. */
 typedef struct {
@@ -94,6 +100,7 @@ typedef struct {
   int32_t renormalize;
   int32_t act_dtype; /* moe_dtype */
   int32_t w_dtype;   /* moe_dtype */
+  float gate_temperature;
 } moe_problem;
 
 /* Host-only, pure helpers (no HIP call).  They return 0 / -1 for a problem
@@ -192,6 +199,42 @@ int32_t moe_expert_down(const moe_problem* p, const void* h, const int32_t* expe
  * atomics. */
 int32_t moe_combine(const moe_problem* p, const void* y_perm, const int32_t* inv_perm,
                     const float* topk_gate, void* y, void* stream);
+
+/* Load statistics of one routing, computed on the device into
+ * stats[MOE_STATS_N] (float32):
+ *   MOE_STAT_MEAN, MOE_STAT_STD: mean and population standard deviation of
+ *       expert_counts over the E experts ("MoE 推理工程深层实战" section 1.2:
+ *       expert load balance is the standard deviation of the tokens each
+ *       expert processes);
+ *   MOE_STAT_MAX_OVER_MEAN: max / mean of expert_counts (chapter 11 section
+ *       11.3.2: 1 is perfectly even, 3-5 is common); 0 when the mean is 0;
+ *   MOE_STAT_DROP_RATE: dropped / (S*K) (section 1.2: token drop rate);
+ *       0 when `dropped` is NULL or S = 0;
+ *   MOE_STAT_AUX_LOSS: alpha * sum_i f_i * P_i (chapter 11 section 11.1.2,
+ *       the balance loss) with f_i = expert_counts[i] / sum(expert_counts)
+ *       and P_i = the mean over the S tokens of softmax(logits[t] / tau)[i],
+ *       tau = p->gate_temperature (0 means 1); 0 when `logits` is NULL or
+ *       there are no counts;
+ *   MOE_STAT_MAX, MOE_STAT_MIN, MOE_STAT_EMPTY: largest and smallest count
+ *       and the number of experts with none.
+ * Arguments (device pointers): expert_counts [E] int32 (as moe_permute
+ * writes them), logits [S][E] float32 (nullable; as moe_route writes them),
+ * dropped [1] int32 (nullable: pairs that were routed to no expert), stats
+ * [MOE_STATS_N] float32 (written).  The sums are taken in a fixed order, so
+ * the result is deterministic.  Needs no workspace. */
+enum {
+  MOE_STAT_MEAN = 0,
+  MOE_STAT_STD = 1,
+  MOE_STAT_MAX_OVER_MEAN = 2,
+  MOE_STAT_DROP_RATE = 3,
+  MOE_STAT_AUX_LOSS = 4,
+  MOE_STAT_MAX = 5,
+  MOE_STAT_MIN = 6,
+  MOE_STAT_EMPTY = 7,
+  MOE_STATS_N = 8
+};
+int32_t moe_load_stats(const moe_problem* p, const int32_t* expert_counts, const float* logits,
+                       const int32_t* dropped, float alpha, float* stats, void* stream);
 
 /* The whole layer: route, permute, expert FFN, combine on one stream.
  *   y [S][d] act.  Optional outputs (nullable): topk_idx_out [S][K],

@@ -48,7 +48,7 @@ __all__ = [
     "decode_bf16", "decode_e4m3fn", "decode", "expert_matrix",
     "router_logits", "softmax", "group_scores_f32", "select_experts",
     "gate_weights", "permute", "gelu", "expert_ffn", "layer_forward",
-    "combine",
+    "combine", "load_stats", "STAT_NAMES",
 ]
 
 
@@ -128,10 +128,11 @@ def router_logits(x: np.ndarray, w_r: np.ndarray, router_bias: Optional[np.ndarr
     return acc.astype(np.float32)
 
 
-def softmax(logits: np.ndarray) -> np.ndarray:
+def softmax(logits: np.ndarray, temperature: float = 1.0) -> np.ndarray:
     """Softmax over experts (last axis) in float64 ([P2] 11.1.1; [P3] routing
-    scores: a probability distribution over the experts)."""
-    z = np.asarray(logits, dtype=np.float64)
+    scores: a probability distribution over the experts).  `temperature` is
+    [P2] 11.3.3's tau: the distribution of exp(s_i / tau), s the scores."""
+    z = np.asarray(logits, dtype=np.float64) / float(temperature)
     z = z - z.max(axis=-1, keepdims=True)
     p = np.exp(z)
     return p / p.sum(axis=-1, keepdims=True)
@@ -188,7 +189,8 @@ def select_experts(logits: np.ndarray, K: int, select_bias: Optional[np.ndarray]
     return order[:, :K].astype(np.int32)
 
 
-def gate_weights(logits: np.ndarray, idx: np.ndarray, renormalize: int = 1) -> np.ndarray:
+def gate_weights(logits: np.ndarray, idx: np.ndarray, renormalize: int = 1,
+                 temperature: float = 1.0) -> np.ndarray:
     """Gate weight of each chosen expert, float64 [S, K].
 
     renormalize=1: softmax restricted to the K chosen (unbiased) logits, so
@@ -196,15 +198,47 @@ def gate_weights(logits: np.ndarray, idx: np.ndarray, renormalize: int = 1) -> n
     other scores to -inf ([P2] 11.1.1), the normalised weighting of [P3]'s
     worked example.  renormalize=0: the chosen experts' probabilities under
     the full softmax, as [P2] section 11.3.1's code multiplies them.
+    Both take the scores divided by `temperature` ([P2] 11.3.3, soft routing:
+    a higher tau spreads the weights more evenly); selection does not use it.
     """
     l = np.asarray(logits, dtype=np.float32).astype(np.float64)
     chosen = np.take_along_axis(l, idx.astype(np.int64), axis=1)
     if renormalize:
-        z = chosen - chosen.max(axis=1, keepdims=True)
-        p = np.exp(z)
-        return p / p.sum(axis=1, keepdims=True)
-    p = softmax(l)
+        return softmax(chosen, temperature)
+    p = softmax(l, temperature)
     return np.take_along_axis(p, idx.astype(np.int64), axis=1)
+
+
+# ---------------------------------------------------------------- statistics
+STAT_NAMES = ("mean", "std", "max_over_mean", "drop_rate", "aux_loss", "max", "min", "empty")
+
+
+def load_stats(counts: np.ndarray, S: int, K: int, logits: Optional[np.ndarray] = None,
+               alpha: float = 1.0, temperature: float = 1.0, dropped: int = 0) -> Dict[str, float]:
+    """Load statistics of one routing, float64.
+
+    [P1] section 1.2: expert load balance is the standard deviation of the
+    tokens each expert processes (taken here over the E per-expert counts,
+    population form) and the token drop rate is the share of routed pairs
+    that overloaded experts dropped (dropped / (S*K)).  [P2] 11.3.2: the
+    evaluation metric is max load / mean load.  [P2] 11.1.2: the balance loss
+    alpha * sum_i f_i * P_i, with f_i the share of the routed assignments
+    that went to expert i and P_i the router's mean probability for expert i
+    over the S tokens (the softmax of the scores, at `temperature`).
+    """
+    c = np.asarray(counts, dtype=np.float64)
+    E = c.size
+    mean = c.sum() / E
+    out = {"mean": mean, "std": float(np.sqrt(((c - mean) ** 2).sum() / E)),
+           "max_over_mean": float(c.max() / mean) if mean > 0 else 0.0,
+           "drop_rate": float(dropped) / (S * K) if S * K > 0 else 0.0,
+           "aux_loss": 0.0, "max": float(c.max()), "min": float(c.min()),
+           "empty": float((c == 0).sum())}
+    if logits is not None and c.sum() > 0 and S > 0:
+        f = c / c.sum()
+        P = softmax(np.asarray(logits, dtype=np.float32), temperature).mean(axis=0)
+        out["aux_loss"] = float(alpha * (f * P).sum())
+    return out
 
 
 # ---------------------------------------------------------------- dispatch
@@ -274,7 +308,7 @@ def combine(gates: np.ndarray, outputs: np.ndarray) -> np.ndarray:
 def layer_forward(x: np.ndarray, w_r: np.ndarray, W1, b1, W2, b2, *, K: int,
                   act: str, w: str, router_bias=None, select_bias=None,
                   n_groups: int = 1, topk_groups: int = 1, renormalize: int = 1,
-                  w1_scale=None, w2_scale=None, logits_in=None,
+                  temperature: float = 1.0, w1_scale=None, w2_scale=None, logits_in=None,
                   tokens: Optional[Sequence[int]] = None,
                   return_parts: bool = False):
     """The whole layer for the tokens `tokens` (default: all), [P2] 11.1.1-2.
@@ -298,7 +332,7 @@ def layer_forward(x: np.ndarray, w_r: np.ndarray, W1, b1, W2, b2, *, K: int,
     else:
         logits = router_logits(xs, decode(w_r, act), router_bias)
     idx = select_experts(logits, K, select_bias, n_groups, topk_groups)
-    gates = gate_weights(logits, idx, renormalize)
+    gates = gate_weights(logits, idx, renormalize, temperature)
     n, d = xs.shape
     outs = np.zeros((n, K, d), dtype=np.float64)
     hidden = {} if return_parts else None

@@ -18,7 +18,7 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "STAGE_ROUTE", "STAGE_PERMUTE", "STAGE_EXPERT_FFN",
     "STAGE_COMBINE", "STAGE_LAYER", "MoEError", "moe_problem", "make_problem", "lib", "LIB_PATH",
     "moe_workspace_bytes", "moe_tile_m", "moe_rows_capacity", "moe_status_string",
-    "workspace", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
+    "workspace", "moe_load_stats", "MOE_STATS_N", "STAT_NAMES", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfl_moe.so")
@@ -26,6 +26,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfl_moe.
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 STAGE_ROUTE, STAGE_PERMUTE, STAGE_EXPERT_FFN, STAGE_COMBINE, STAGE_LAYER = 0, 1, 2, 3, 4
+# moe_load_stats outputs, in order (MOE_STAT_* in include/moe.h)
+STAT_NAMES = ("mean", "std", "max_over_mean", "drop_rate", "aux_loss", "max", "min", "empty")
+MOE_STATS_N = len(STAT_NAMES)
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3,
        torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3}
@@ -42,13 +45,14 @@ class moe_problem(ctypes.Structure):
     _fields_ = [("S", ctypes.c_int64), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("topk_groups", ctypes.c_int32), ("renormalize", ctypes.c_int32),
-                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32)]
+                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+                ("gate_temperature", ctypes.c_float)]
 
 
 def make_problem(S, d, d_ff, E, K, act="bf16", w="bf16", n_groups=1, topk_groups=1,
-                 renormalize=1) -> moe_problem:
+                 renormalize=1, temperature=1.0) -> moe_problem:
     return moe_problem(int(S), int(d), int(d_ff), int(E), int(K), int(n_groups), int(topk_groups),
-                       int(renormalize), _DT[act], _DT[w])
+                       int(renormalize), _DT[act], _DT[w], float(temperature))
 
 
 _lib = None
@@ -67,6 +71,7 @@ _SIGS = {
     "moe_expert_down": (_i32, [_P] + [_vp] * 7 + [_vp, _sz, _vp]),
     "moe_combine": (_i32, [_P] + [_vp] * 4 + [_vp]),
     "moe_layer_forward": (_i32, [_P] + [_vp] * 15 + [_vp, _sz, _vp]),
+    "moe_load_stats": (_i32, [_P, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]),
 }
 
 
@@ -231,3 +236,14 @@ def moe_layer_forward(p, x, W_r, W1, b1, W2, b2, router_bias=None, select_bias=N
                                  _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_layer_forward", st)
     return y
+
+
+def moe_load_stats(p, expert_counts, logits=None, dropped=None, alpha=1.0, stats=None, stream=None):
+    """Load statistics of one routing as a float32 tensor [MOE_STATS_N] on the
+    device, in the order of STAT_NAMES (see moe_load_stats in include/moe.h)."""
+    if stats is None:
+        stats = torch.zeros(MOE_STATS_N, dtype=torch.float32, device=expert_counts.device)
+    st = lib().moe_load_stats(ctypes.byref(p), _ptr(expert_counts), _ptr(logits), _ptr(dropped),
+                              float(alpha), _ptr(stats), _stream(stream))
+    _check("moe_load_stats", st)
+    return stats

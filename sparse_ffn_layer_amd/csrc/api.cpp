@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <initializer_list>
 
 #include "common.h"
@@ -29,6 +30,8 @@ hipError_t launch_expert_down(const Problem&, int64_t, const void*, const int32_
 size_t expert_split_bytes(const Problem& p);
 hipError_t launch_combine(const Problem&, const void*, const int32_t*, const float*, void*,
                           hipStream_t);
+hipError_t launch_load_stats(const Problem&, const int32_t*, const float*, const int32_t*, float,
+                             float*, hipStream_t);
 int gemm_tile_m(const Problem& p);
 }  // namespace sfl
 
@@ -48,6 +51,9 @@ int32_t check_problem(const moe_problem* mp, Problem* out) {
   if (q.S < 0 || q.d < 1 || q.d_ff < 1 || q.E < 1 || q.K < 1 || q.K > q.E)
     return MOE_ERR_INVALID_ARG;
   if (q.renormalize != 0 && q.renormalize != 1) return MOE_ERR_INVALID_ARG;
+  // gate temperature: 0 means 1; otherwise positive and finite (NaN fails too)
+  const float tau = q.gate_temperature == 0.f ? 1.f : q.gate_temperature;
+  if (!(tau > 0.f) || !(tau < INFINITY)) return MOE_ERR_INVALID_ARG;
   if (q.act_dtype < MOE_F32 || q.act_dtype > MOE_FP8_E4M3 || q.w_dtype < MOE_F32 ||
       q.w_dtype > MOE_FP8_E4M3)
     return MOE_ERR_INVALID_ARG;
@@ -69,6 +75,7 @@ int32_t check_problem(const moe_problem* mp, Problem* out) {
     out->n_groups = q.n_groups > 1 ? q.n_groups : 1;
     out->topk_groups = q.n_groups > 1 ? q.topk_groups : 1;
     out->renormalize = q.renormalize; out->act = q.act_dtype; out->w = q.w_dtype;
+    out->inv_tau = 1.f / tau;
   }
   return MOE_OK;
 }
@@ -294,6 +301,19 @@ int32_t moe_combine(const moe_problem* mp, const void* y_perm, const int32_t* in
   for (const void* q : ptrs)
     if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_combine(p, y_perm, inv_perm, topk_gate, y, (hipStream_t)stream));
+}
+
+int32_t moe_load_stats(const moe_problem* mp, const int32_t* expert_counts, const float* logits,
+                       const int32_t* dropped, float alpha, float* stats, void* stream) {
+  Problem p;
+  int32_t s = check_problem(mp, &p);
+  if (s != MOE_OK) return s;
+  if (!std::isfinite(alpha)) return MOE_ERR_INVALID_ARG;
+  if (p.S == 0) return MOE_OK;
+  if (expert_counts == nullptr || stats == nullptr) return MOE_ERR_INVALID_ARG;
+  for (const void* q : {(const void*)expert_counts, (const void*)logits, (const void*)dropped, (const void*)stats})
+    if (q != nullptr && !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_load_stats(p, expert_counts, logits, dropped, alpha, stats, (hipStream_t)stream));
 }
 
 int32_t moe_layer_forward(const moe_problem* mp, const void* x, const void* W_r,

@@ -12,6 +12,7 @@ struct Problem {
   int d, d_ff, E, K;
   int n_groups, topk_groups, renormalize;
   int act, w;  // moe_dtype values
+  float inv_tau;  // 1 / gate temperature
 };
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };

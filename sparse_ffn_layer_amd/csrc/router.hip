@@ -18,16 +18,21 @@
 // group's experts in index order.
 #include "common.h"
 
+#include <climits>
+
 namespace sfl {
 
 constexpr int ROUTER_WAVES = 4;  // tokens per 256-thread block
 
 // Select K experts from this token's logits and write indices and gates.
 // lg[r]: unbiased logit of expert r*64 + lane (-inf where that is >= E).
+// The gates use logit / tau (inv_tau = 1 / tau; section 11.3.3's soft
+// routing temperature); at tau = 1 the product is exact, so plain gates are
+// unchanged.  Selection does not depend on tau.
 template <int R>
 __device__ __forceinline__ void select_and_gate(const float (&lg)[R], int E, int K,
                                                 const float* __restrict__ sbias, int n_groups,
-                                                int topk_groups, int renorm, int64_t t,
+                                                int topk_groups, int renorm, float inv_tau, int64_t t,
                                                 int32_t* __restrict__ idx_out,
                                                 float* __restrict__ gate_out) {
   const int lane = lane_id();
@@ -113,7 +118,7 @@ __device__ __forceinline__ void select_and_gate(const float (&lg)[R], int E, int
   float g;
   if (renorm) {
     const float mx = wave_max(lane < K ? my_l : -INFINITY);
-    const float ex = lane < K ? expf(my_l - mx) : 0.f;
+    const float ex = lane < K ? expf((my_l - mx) * inv_tau) : 0.f;
     g = ex / wave_sum(ex);
   } else {
     float mx = -INFINITY;
@@ -122,9 +127,9 @@ __device__ __forceinline__ void select_and_gate(const float (&lg)[R], int E, int
     mx = wave_max(mx);
     float z = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) z += (r * 64 + lane < E) ? expf(lg[r] - mx) : 0.f;
+    for (int r = 0; r < R; ++r) z += (r * 64 + lane < E) ? expf((lg[r] - mx) * inv_tau) : 0.f;
     z = wave_sum(z);
-    g = expf(my_l - mx) / z;
+    g = expf((my_l - mx) * inv_tau) / z;
   }
   if (lane < K) {
     idx_out[t * K + lane] = my_e;
@@ -139,7 +144,7 @@ __global__ void __launch_bounds__(64 * ROUTER_WAVES)
 router_fused_kernel(int64_t S, int d, int E, int K, const T* __restrict__ x,
                     const T* __restrict__ Wr, const float* __restrict__ rbias,
                     const float* __restrict__ sbias, int n_groups, int topk_groups, int renorm,
-                    float* __restrict__ logits_out, int32_t* __restrict__ idx,
+                    float inv_tau, float* __restrict__ logits_out, int32_t* __restrict__ idx,
                     float* __restrict__ gate) {
   const int lane = lane_id();
   const int64_t t = (int64_t)blockIdx.x * ROUTER_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -204,7 +209,7 @@ router_fused_kernel(int64_t S, int d, int E, int K, const T* __restrict__ x,
     for (int r = 0; r < R; ++r)
       if (r * 64 + lane < E) logits_out[t * E + r * 64 + lane] = lg[r];
   }
-  select_and_gate<R>(lg, E, K, sbias, n_groups, topk_groups, renorm, t, idx, gate);
+  select_and_gate<R>(lg, E, K, sbias, n_groups, topk_groups, renorm, inv_tau, t, idx, gate);
 }
 
 // Selection from precomputed float32 scores [S][E].
@@ -212,7 +217,7 @@ template <int R>
 __global__ void __launch_bounds__(64 * ROUTER_WAVES)
 route_logits_kernel(int64_t S, int E, int K, const float* __restrict__ logits,
                     const float* __restrict__ sbias, int n_groups, int topk_groups, int renorm,
-                    float* __restrict__ logits_copy, int32_t* __restrict__ idx,
+                    float inv_tau, float* __restrict__ logits_copy, int32_t* __restrict__ idx,
                     float* __restrict__ gate) {
   const int lane = lane_id();
   const int64_t t = (int64_t)blockIdx.x * ROUTER_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -224,7 +229,127 @@ route_logits_kernel(int64_t S, int E, int K, const float* __restrict__ logits,
     lg[r] = e < E ? logits[t * E + e] : -INFINITY;
     if (logits_copy != nullptr && e < E) logits_copy[t * E + e] = lg[r];
   }
-  select_and_gate<R>(lg, E, K, sbias, n_groups, topk_groups, renorm, t, idx, gate);
+  select_and_gate<R>(lg, E, K, sbias, n_groups, topk_groups, renorm, inv_tau, t, idx, gate);
+}
+
+// ------------------------------------------------------------------ statistics
+// Load statistics of one routing, one workgroup of 16 waves.  Counts: thread
+// e reads expert e's count; sums in a fixed tree order.  Aux loss: wave w
+// takes tokens w, w + 16, ... in order and accumulates softmax(logits / tau)
+// per expert in its registers; the 16 partial sums are added in wave order.
+// Every sum has a fixed order, so the result is deterministic.
+constexpr int STATS_WAVES = 16;
+template <int R>
+__global__ void __launch_bounds__(64 * STATS_WAVES)
+load_stats_kernel(int64_t S, int E, int K, const int32_t* __restrict__ counts,
+                  const float* __restrict__ logits, const int32_t* __restrict__ dropped, float alpha,
+                  float inv_tau, float* __restrict__ stats) {
+  __shared__ float red[64 * STATS_WAVES];
+  __shared__ int ired[64 * STATS_WAVES];
+  __shared__ float pexp[STATS_WAVES][R * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // ---- counts: sum, max, min, empty (exact integers), then sum of squares
+  int c = tid < E ? counts[tid] : 0;
+  auto tree_i = [&](int v, int op) -> int {  // op 0: sum, 1: max, 2: min
+    ired[tid] = v;
+    __syncthreads();
+    for (int w = 64 * STATS_WAVES / 2; w >= 1; w >>= 1) {
+      if (tid < w) {
+        const int o = ired[tid + w];
+        ired[tid] = op == 0 ? ired[tid] + o : op == 1 ? max(ired[tid], o) : min(ired[tid], o);
+      }
+      __syncthreads();
+    }
+    const int r = ired[0];
+    __syncthreads();
+    return r;
+  };
+  auto tree_f = [&](float v) -> float {
+    red[tid] = v;
+    __syncthreads();
+    for (int w = 64 * STATS_WAVES / 2; w >= 1; w >>= 1) {
+      if (tid < w) red[tid] += red[tid + w];
+      __syncthreads();
+    }
+    const float r = red[0];
+    __syncthreads();
+    return r;
+  };
+  const int total = tree_i(c, 0);
+  const int cmax = tree_i(tid < E ? c : INT_MIN, 1);
+  const int cmin = tree_i(tid < E ? c : INT_MAX, 2);
+  const int empty = tree_i(tid < E && c == 0 ? 1 : 0, 0);
+  const float mean = (float)total / (float)E;
+  const float dev = tid < E ? (float)c - mean : 0.f;
+  const float var = tree_f(dev * dev) / (float)E;
+
+  // ---- aux loss: P_i = mean over tokens of softmax(logits[t] / tau)[i]
+  float aux = 0.f;
+  if (logits != nullptr && total > 0 && S > 0) {
+    float p[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) p[r] = 0.f;
+    for (int64_t t = wave; t < S; t += STATS_WAVES) {
+      float l[R];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int e = r * 64 + lane;
+        l[r] = e < E ? logits[t * E + e] : -INFINITY;
+        mx = fmaxf(mx, l[r]);
+      }
+      mx = wave_max(mx);
+      float z = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        l[r] = (r * 64 + lane < E) ? expf((l[r] - mx) * inv_tau) : 0.f;
+        z += l[r];
+      }
+      z = wave_sum(z);
+      const float iz = 1.f / z;
+#pragma unroll
+      for (int r = 0; r < R; ++r) p[r] += l[r] * iz;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) pexp[wave][r * 64 + lane] = p[r];
+    __syncthreads();
+    float term = 0.f;
+    if (tid < E) {
+      float P = 0.f;
+      for (int w = 0; w < STATS_WAVES; ++w) P += pexp[w][tid];  // wave order
+      P /= (float)S;
+      term = ((float)c / (float)total) * P;
+    }
+    aux = alpha * tree_f(term);
+  }
+  if (tid == 0) {
+    const int64_t pairs = S * (int64_t)K;
+    const int drop = dropped != nullptr ? dropped[0] : 0;
+    stats[0] = mean;
+    stats[1] = sqrtf(var);
+    stats[2] = mean > 0.f ? (float)cmax / mean : 0.f;
+    stats[3] = pairs > 0 ? (float)drop / (float)pairs : 0.f;
+    stats[4] = aux;
+    stats[5] = (float)cmax;
+    stats[6] = (float)cmin;
+    stats[7] = (float)empty;
+  }
+}
+
+hipError_t launch_load_stats(const Problem& p, const int32_t* counts, const float* logits,
+                             const int32_t* dropped, float alpha, float* stats, hipStream_t st) {
+  const int R = (p.E + 63) / 64;
+  const dim3 grid(1), block(64 * STATS_WAVES);
+#define SFL_STATS(RR) \
+  load_stats_kernel<RR><<<grid, block, 0, st>>>(p.S, p.E, p.K, counts, logits, dropped, alpha, p.inv_tau, stats)
+  switch (R) {
+    case 1: SFL_STATS(1); break;
+    case 2: SFL_STATS(2); break;
+    case 3: case 4: SFL_STATS(4); break;
+    default: SFL_STATS(8); break;
+  }
+#undef SFL_STATS
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ launchers
@@ -237,8 +362,8 @@ static hipError_t launch_fused_T(const Problem& p, const void* x, const void* Wr
 #define SFL_FUSED(RR)                                                                           \
   router_fused_kernel<T, EC, RR><<<grid, block, 0, st>>>(p.S, p.d, p.E, p.K, (const T*)x,      \
                                                          (const T*)Wr, rb, sb, p.n_groups,      \
-                                                         p.topk_groups, p.renormalize, lo, idx, \
-                                                         gate)
+                                                         p.topk_groups, p.renormalize, p.inv_tau, \
+                                                         lo, idx, gate)
   switch (R) {
     case 1: SFL_FUSED(1); break;
     case 2: SFL_FUSED(2); break;
@@ -266,8 +391,8 @@ hipError_t launch_route_logits(const Problem& p, const float* logits, const floa
   const dim3 grid((unsigned)ceil_div(p.S, ROUTER_WAVES)), block(64 * ROUTER_WAVES);
 #define SFL_ROUTE(RR)                                                                         \
   route_logits_kernel<RR><<<grid, block, 0, st>>>(p.S, p.E, p.K, logits, sb, p.n_groups,     \
-                                                  p.topk_groups, p.renormalize, logits_copy, \
-                                                  idx, gate)
+                                                  p.topk_groups, p.renormalize, p.inv_tau,   \
+                                                  logits_copy, idx, gate)
   switch (R) {
     case 1: SFL_ROUTE(1); break;
     case 2: SFL_ROUTE(2); break;

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -40,11 +40,11 @@ def test_struct_layout_matches_header():
 #include <stdio.h>
 #include "moe.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_problem),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_problem),
     offsetof(moe_problem, S), offsetof(moe_problem, d), offsetof(moe_problem, d_ff),
     offsetof(moe_problem, E), offsetof(moe_problem, K), offsetof(moe_problem, n_groups),
     offsetof(moe_problem, topk_groups), offsetof(moe_problem, renormalize),
-    offsetof(moe_problem, act_dtype), offsetof(moe_problem, w_dtype));
+    offsetof(moe_problem, act_dtype), offsetof(moe_problem, w_dtype), offsetof(moe_problem, gate_temperature));
   return 0;
 }'''
     with tempfile.TemporaryDirectory() as d:
@@ -98,6 +98,28 @@ def test_invalid_problems_rejected(kw, status):
     assert lib.moe_combine(ctypes.byref(p), *([fake] * 4), None) == status
     assert lib.moe_expert_up(ctypes.byref(p), *([fake] * 7), None, 0, None) == status
     assert lib.moe_expert_down(ctypes.byref(p), *([fake] * 7), None, 0, None) == status
+
+
+@pytest.mark.parametrize("tau,ok", [(0.0, True), (1.0, True), (0.25, True), (-1.0, False),
+                                    (float("nan"), False), (float("inf"), False)])
+def test_gate_temperature_validation(tau, ok):
+    """0 means 1; a temperature must otherwise be positive and finite."""
+    p = prob(temperature=tau)
+    lib = M.lib()
+    assert (lib.moe_tile_m(ctypes.byref(p)) > 0) == ok
+    if not ok:
+        assert lib.moe_route(ctypes.byref(p), *([ctypes.c_void_p(1 << 20)] * 8), None, 0, None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_load_stats_argument_checks():
+    lib = M.lib()
+    p = prob()
+    a = ctypes.c_void_p(1 << 20)
+    assert lib.moe_load_stats(ctypes.byref(p), None, None, None, 1.0, a, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(ctypes.byref(p), a, None, None, 1.0, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(ctypes.byref(p), a, None, None, float("nan"), a, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 4), None, None, 1.0, a, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(ctypes.byref(prob(S=0)), None, None, None, 1.0, None, None) == M.MOE_OK
 
 
 def test_null_problem_and_status_strings():
