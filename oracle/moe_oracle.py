@@ -35,6 +35,9 @@ Readings where the pages are silent or ambiguous (each is stated where used):
   * GeLU is the exact x*Phi(x) with erf.
   * The selection-only bias (P1 section 2.3) enters the keys; gates use the
     unbiased logits.
+  * Capacity-limited dispatch (P2 11.3.3, P1 sections 1.2 and 2.2 leave the
+    rule open): rounds of in-order acceptance, rejected pairs move to the
+    token's best expert that still has room; see apply_capacity.
 """
 from __future__ import annotations
 
@@ -48,7 +51,7 @@ __all__ = [
     "decode_bf16", "decode_e4m3fn", "decode", "expert_matrix",
     "router_logits", "softmax", "group_scores_f32", "select_experts",
     "gate_weights", "permute", "gelu", "expert_ffn", "layer_forward",
-    "combine", "load_stats", "STAT_NAMES",
+    "combine", "load_stats", "STAT_NAMES", "selection_keys", "apply_capacity",
 ]
 
 
@@ -207,6 +210,98 @@ def gate_weights(logits: np.ndarray, idx: np.ndarray, renormalize: int = 1,
         return softmax(chosen, temperature)
     p = softmax(l, temperature)
     return np.take_along_axis(p, idx.astype(np.int64), axis=1)
+
+
+# ---------------------------------------------------------------- capacity
+def selection_keys(logits: np.ndarray, select_bias: Optional[np.ndarray] = None, n_groups: int = 1,
+                   topk_groups: int = 1) -> np.ndarray:
+    """The float32 keys select_experts ranks, with -inf for experts outside
+    the token's kept groups (the same steps as select_experts)."""
+    key = np.asarray(logits, dtype=np.float32)
+    if select_bias is not None:
+        key = (key + np.asarray(select_bias, dtype=np.float32)[None, :]).astype(np.float32)
+    S, E = key.shape
+    if n_groups > 1:
+        gs = group_scores_f32(key, n_groups)
+        g_order = np.argsort(-gs, axis=1, kind="stable")[:, :topk_groups]
+        keep = np.zeros((S, n_groups), dtype=bool)
+        np.put_along_axis(keep, g_order, True, axis=1)
+        key = np.where(np.repeat(keep, E // n_groups, axis=1), key, np.float32(-np.inf)).astype(np.float32)
+    return key
+
+
+def apply_capacity(logits: np.ndarray, idx: np.ndarray, capacity: int,
+                   select_bias: Optional[np.ndarray] = None, n_groups: int = 1, topk_groups: int = 1,
+                   renormalize: int = 1, temperature: float = 1.0):
+    """Capacity-limited dispatch: each expert takes at most `capacity` of the
+    routed (token, slot) pairs; pairs past the limit go to the next-best
+    expert, and are dropped when none has room ([P2] 11.3.3, expert dropping:
+    the excess of an overloaded expert moves to the next-best expert; [P1]
+    section 1.2, token drop rate: the share of tokens lost to overloaded
+    experts; [P1] section 2.2: tokens past a buffer's capacity are dropped or
+    held back in an overflow buffer).
+
+    The pages leave the rule open; the reading taken:
+      * rounds: every pending pair proposes its current expert; an expert
+        accepts proposals in (token, slot) order while it has room;
+      * a rejected pair moves to the best expert of its token's ranking (the
+        selection keys of select_experts, kept groups only; key descending,
+        lower index on ties) that the token does not hold in another
+        accepted or pending slot and that still has room; the token's slots
+        are taken in slot order, so two of them never pick the same expert;
+        with no such expert the pair is dropped (index -1);
+      * a slot keeps its position; the gates are those of gate_weights over
+        the token's kept slots (dropped slots get 0).
+    Each round with a rejection fills at least one more expert, so it ends.
+    capacity 0 means no limit.  Input indices outside [0, E) count as
+    dropped pairs.  Returns (idx [S,K] int32, gates [S,K] float64, number of
+    pairs with index -1).
+    """
+    if capacity < 0:
+        raise ValueError("capacity must be >= 0")
+    if capacity == 0:                           # no limit
+        capacity = np.iinfo(np.int64).max
+    key = selection_keys(logits, select_bias, n_groups, topk_groups)
+    S, E = key.shape
+    K = idx.shape[1]
+    ranking = np.argsort(-key, axis=1, kind="stable")
+    allowed = key > -np.inf
+    cur = np.asarray(idx, dtype=np.int64).copy()
+    cur[(cur < 0) | (cur >= E)] = -1            # pairs routed to no expert stay dropped
+    PENDING, ACCEPTED, REJECTED, DROPPED = 0, 1, 2, 3
+    state = np.where(cur >= 0, PENDING, DROPPED)
+    dropped = int((cur < 0).sum())
+    load = np.zeros(E, dtype=np.int64)
+    while (state == PENDING).any():
+        for t in range(S):                      # acceptance in (token, slot) order
+            for k in range(K):
+                if state[t, k] == PENDING:
+                    e = cur[t, k]
+                    if load[e] < capacity:
+                        load[e] += 1
+                        state[t, k] = ACCEPTED
+                    else:
+                        state[t, k] = REJECTED
+        for t in range(S):                      # rerouting
+            for k in range(K):
+                if state[t, k] != REJECTED:
+                    continue
+                held = {int(cur[t, j]) for j in range(K)
+                        if j != k and state[t, j] in (PENDING, ACCEPTED)}
+                nxt = [int(e) for e in ranking[t] if allowed[t, e] and int(e) not in held and load[e] < capacity]
+                if nxt:
+                    cur[t, k] = nxt[0]
+                    state[t, k] = PENDING
+                else:
+                    cur[t, k] = -1
+                    state[t, k] = DROPPED
+                    dropped += 1
+    gates = np.zeros((S, K), dtype=np.float64)
+    for t in range(S):
+        kept = np.nonzero(cur[t] >= 0)[0]
+        if kept.size:
+            gates[t, kept] = gate_weights(logits[t:t + 1], cur[t:t + 1, kept], renormalize, temperature)[0]
+    return cur.astype(np.int32), gates, dropped
 
 
 # ---------------------------------------------------------------- statistics
