@@ -71,7 +71,8 @@ typedef enum {
   MOE_STAGE_PERMUTE = 1,
   MOE_STAGE_EXPERT_FFN = 2,
   MOE_STAGE_COMBINE = 3,
-  MOE_STAGE_LAYER = 4
+  MOE_STAGE_LAYER = 4,
+  MOE_STAGE_CAPACITY = 5
 } moe_stage;
 
 /* The problem statement: S tokens of width d (S = batch x sequence, chapter
@@ -87,6 +88,9 @@ typedef enum {
  *    depend on it.  0 means 1 (so a zero-initialised problem keeps plain
  *    gates); tau must otherwise be positive and finite, else
  *    MOE_ERR_INVALID_ARG.
+ *  - capacity: the most (token, slot) pairs one expert takes in
+ *    moe_layer_forward and moe_apply_capacity (chapter 11 section 11.3.3,
+ *    expert dropping); 0 = no limit; negative: MOE_ERR_INVALID_ARG.
  *  - Limits: 1 <= E <= 512, 1 <= K <= min(E, 64), d and d_ff multiples of 64,
  *    S < 2^31 / K.  Outside them: MOE_ERR_UNSUPPORTED. */
 typedef struct {
@@ -101,6 +105,7 @@ typedef struct {
   int32_t act_dtype; /* moe_dtype */
   int32_t w_dtype;   /* moe_dtype */
   float gate_temperature;
+  int32_t capacity;
 } moe_problem;
 
 /* Host-only, pure helpers (no HIP call).  They return 0 / -1 for a problem
@@ -236,9 +241,44 @@ enum {
 int32_t moe_load_stats(const moe_problem* p, const int32_t* expert_counts, const float* logits,
                        const int32_t* dropped, float alpha, float* stats, void* stream);
 
+/* Capacity-limited dispatch (chapter 11 section 11.3.3, expert dropping:
+ * the excess of an overloaded expert moves to the next-best expert;
+ * "MoE 推理工程深层实战" sections 1.2 and 2.2: token drop rate, tokens past a
+ * buffer's capacity are dropped).  The pages leave the rule open; it is:
+ *  - rounds: every pending (token, slot) pair proposes its current expert;
+ *    the expert accepts proposals in (token, slot) order while it holds
+ *    fewer than p->capacity pairs;
+ *  - a rejected pair moves to the best expert in its token's selection order
+ *    (logit + select_bias, eligible groups only, key descending, lower index
+ *    on ties; the order moe_route uses) that has room and that the token
+ *    does not hold in another accepted or pending slot; a token's rejected
+ *    slots are taken in slot order; with no such expert the pair is dropped
+ *    (index -1);
+ *  - a slot keeps its position; gates are recomputed over each token's kept
+ *    slots as moe_route computes them (dropped slots get 0), so a token that
+ *    keeps all its slots keeps its gates bit for bit.
+ * p->capacity = 0 means no limit (nothing moves).
+ *   logits [S][E] float32: the router scores (as moe_route's logits_out).
+ *   select_bias [E] (nullable): the selection-only bias moe_route used.
+ *   topk_idx [S][K] int32, in/out: the routing on entry (indices outside
+ *       [0, E) count as dropped pairs and become -1); the capacity-limited
+ *       routing on return.
+ *   topk_gate [S][K] float32, out.
+ *   dropped [1] int32 (nullable): pairs with index -1 on return.
+ *   ws: moe_workspace_bytes(p, MOE_STAGE_CAPACITY) bytes.
+ * moe_permute, moe_combine and moe_load_stats accept the -1 entries.  One
+ * workgroup runs the rounds (at most E + 1), so the call costs more than
+ * moe_route for large S; the result is deterministic. */
+int32_t moe_apply_capacity(const moe_problem* p, const float* logits, const float* select_bias,
+                           int32_t* topk_idx, float* topk_gate, int32_t* dropped, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* The whole layer: route, permute, expert FFN, combine on one stream.
  *   y [S][d] act.  Optional outputs (nullable): topk_idx_out [S][K],
  *   topk_gate_out [S][K], logits_out [S][E], expert_counts_out [E].
+ *   With p->capacity > 0 the routing passes through moe_apply_capacity's
+ *   rule before the permute; dropped pairs then have topk_idx -1 and the
+ *   dropped count is S*K minus the sum of expert_counts_out.
  *   ws: moe_workspace_bytes(p, MOE_STAGE_LAYER) bytes. */
 int32_t moe_layer_forward(const moe_problem* p, const void* x, const void* W_r,
                           const float* router_bias, const float* select_bias,

@@ -404,7 +404,7 @@ def layer_forward(x: np.ndarray, w_r: np.ndarray, W1, b1, W2, b2, *, K: int,
                   act: str, w: str, router_bias=None, select_bias=None,
                   n_groups: int = 1, topk_groups: int = 1, renormalize: int = 1,
                   temperature: float = 1.0, w1_scale=None, w2_scale=None, logits_in=None,
-                  tokens: Optional[Sequence[int]] = None,
+                  tokens: Optional[Sequence[int]] = None, capacity: int = 0,
                   return_parts: bool = False):
     """The whole layer for the tokens `tokens` (default: all), [P2] 11.1.1-2.
 
@@ -413,6 +413,9 @@ def layer_forward(x: np.ndarray, w_r: np.ndarray, W1, b1, W2, b2, *, K: int,
     only the experts in use are read); b1 [E][d_ff], b2 [E][d] of dtype
     `act`; w1_scale [E][d_ff], w2_scale [E][d] float32 for fp8 weights.
     logits_in [S,E] float32 replaces the router product when given.
+    capacity > 0 limits each expert to that many (token, slot) pairs with
+    apply_capacity; that rule looks at every token, so the routing is then
+    computed for all S tokens before `tokens` are picked.
 
     Steps: router logits -> selection -> gates -> for each expert in index
     order, the expert FFN of every (token, slot) pair routed to it -> gate
@@ -422,16 +425,26 @@ def layer_forward(x: np.ndarray, w_r: np.ndarray, W1, b1, W2, b2, *, K: int,
     S = x.shape[0]
     tok = np.arange(S) if tokens is None else np.asarray(tokens, dtype=np.int64)
     xs = decode(np.asarray(x)[tok], act)
-    if logits_in is not None:
-        logits = np.asarray(logits_in, dtype=np.float32)[tok]
+    if capacity:
+        if logits_in is not None:
+            full = np.asarray(logits_in, dtype=np.float32)
+        else:
+            full = router_logits(decode(np.asarray(x), act), decode(w_r, act), router_bias)
+        idx_all = select_experts(full, K, select_bias, n_groups, topk_groups)
+        idx_all, gates_all, _ = apply_capacity(full, idx_all, capacity, select_bias, n_groups,
+                                               topk_groups, renormalize, temperature)
+        logits, idx, gates = full[tok], idx_all[tok], gates_all[tok]
     else:
-        logits = router_logits(xs, decode(w_r, act), router_bias)
-    idx = select_experts(logits, K, select_bias, n_groups, topk_groups)
-    gates = gate_weights(logits, idx, renormalize, temperature)
+        if logits_in is not None:
+            logits = np.asarray(logits_in, dtype=np.float32)[tok]
+        else:
+            logits = router_logits(xs, decode(w_r, act), router_bias)
+        idx = select_experts(logits, K, select_bias, n_groups, topk_groups)
+        gates = gate_weights(logits, idx, renormalize, temperature)
     n, d = xs.shape
     outs = np.zeros((n, K, d), dtype=np.float64)
     hidden = {} if return_parts else None
-    for e in np.unique(idx):                 # experts in index order
+    for e in np.unique(idx[idx >= 0]):       # experts in index order; dropped pairs add nothing
         rows, slots = np.nonzero(idx == e)   # pairs routed to e, token order
         s1 = None if w1_scale is None else w1_scale[e]
         s2 = None if w2_scale is None else w2_scale[e]

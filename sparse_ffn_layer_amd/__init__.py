@@ -18,14 +18,14 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "STAGE_ROUTE", "STAGE_PERMUTE", "STAGE_EXPERT_FFN",
     "STAGE_COMBINE", "STAGE_LAYER", "MoEError", "moe_problem", "make_problem", "lib", "LIB_PATH",
     "moe_workspace_bytes", "moe_tile_m", "moe_rows_capacity", "moe_status_string",
-    "workspace", "moe_load_stats", "MOE_STATS_N", "STAT_NAMES", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
+    "workspace", "moe_load_stats", "moe_apply_capacity", "STAGE_CAPACITY", "MOE_STATS_N", "STAT_NAMES", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfl_moe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
-STAGE_ROUTE, STAGE_PERMUTE, STAGE_EXPERT_FFN, STAGE_COMBINE, STAGE_LAYER = 0, 1, 2, 3, 4
+STAGE_ROUTE, STAGE_PERMUTE, STAGE_EXPERT_FFN, STAGE_COMBINE, STAGE_LAYER, STAGE_CAPACITY = 0, 1, 2, 3, 4, 5
 # moe_load_stats outputs, in order (MOE_STAT_* in include/moe.h)
 STAT_NAMES = ("mean", "std", "max_over_mean", "drop_rate", "aux_loss", "max", "min", "empty")
 MOE_STATS_N = len(STAT_NAMES)
@@ -46,13 +46,13 @@ class moe_problem(ctypes.Structure):
                 ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("topk_groups", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
-                ("gate_temperature", ctypes.c_float)]
+                ("gate_temperature", ctypes.c_float), ("capacity", ctypes.c_int32)]
 
 
 def make_problem(S, d, d_ff, E, K, act="bf16", w="bf16", n_groups=1, topk_groups=1,
-                 renormalize=1, temperature=1.0) -> moe_problem:
+                 renormalize=1, temperature=1.0, capacity=0) -> moe_problem:
     return moe_problem(int(S), int(d), int(d_ff), int(E), int(K), int(n_groups), int(topk_groups),
-                       int(renormalize), _DT[act], _DT[w], float(temperature))
+                       int(renormalize), _DT[act], _DT[w], float(temperature), int(capacity))
 
 
 _lib = None
@@ -72,6 +72,7 @@ _SIGS = {
     "moe_combine": (_i32, [_P] + [_vp] * 4 + [_vp]),
     "moe_layer_forward": (_i32, [_P] + [_vp] * 15 + [_vp, _sz, _vp]),
     "moe_load_stats": (_i32, [_P, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]),
+    "moe_apply_capacity": (_i32, [_P] + [_vp] * 5 + [_vp, _sz, _vp]),
 }
 
 
@@ -247,3 +248,19 @@ def moe_load_stats(p, expert_counts, logits=None, dropped=None, alpha=1.0, stats
                               float(alpha), _ptr(stats), _stream(stream))
     _check("moe_load_stats", st)
     return stats
+
+
+def moe_apply_capacity(p, logits, topk_idx, select_bias=None, topk_gate=None, dropped=None, ws=None,
+                       stream=None):
+    """Capacity-limited dispatch with p.capacity pairs per expert; topk_idx
+    is updated in place.  Returns (topk_idx, topk_gate, dropped[1])."""
+    if topk_gate is None:
+        topk_gate = torch.empty((p.S, p.K), dtype=torch.float32, device=topk_idx.device)
+    if dropped is None:
+        dropped = torch.zeros(4, dtype=torch.int32, device=topk_idx.device)
+    if ws is None:
+        ws = workspace(p, STAGE_CAPACITY, topk_idx.device)
+    st = lib().moe_apply_capacity(ctypes.byref(p), _ptr(logits), _ptr(select_bias), _ptr(topk_idx),
+                                  _ptr(topk_gate), _ptr(dropped), _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_apply_capacity", st)
+    return topk_idx, topk_gate, dropped[:1]

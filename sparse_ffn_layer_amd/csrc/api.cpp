@@ -11,7 +11,7 @@
 #include "common.h"
 
 namespace sfl {
-// kernels (router.hip, permute.hip, gemm.hip, combine.hip)
+// kernels (router.hip, capacity.hip, permute.hip, gemm.hip, combine.hip)
 hipError_t launch_router_fused(const Problem&, const void*, const void*, const float*,
                                const float*, float*, int32_t*, float*, hipStream_t);
 hipError_t launch_route_logits(const Problem&, const float*, const float*, float*, int32_t*,
@@ -32,6 +32,9 @@ hipError_t launch_combine(const Problem&, const void*, const int32_t*, const flo
                           hipStream_t);
 hipError_t launch_load_stats(const Problem&, const int32_t*, const float*, const int32_t*, float,
                              float*, hipStream_t);
+hipError_t launch_capacity(const Problem&, int, const float*, const float*, int32_t*, float*,
+                           int32_t*, int32_t*, hipStream_t);
+size_t capacity_scratch_ints(int64_t pairs);
 int gemm_tile_m(const Problem& p);
 }  // namespace sfl
 
@@ -54,6 +57,7 @@ int32_t check_problem(const moe_problem* mp, Problem* out) {
   // gate temperature: 0 means 1; otherwise positive and finite (NaN fails too)
   const float tau = q.gate_temperature == 0.f ? 1.f : q.gate_temperature;
   if (!(tau > 0.f) || !(tau < INFINITY)) return MOE_ERR_INVALID_ARG;
+  if (q.capacity < 0) return MOE_ERR_INVALID_ARG;
   if (q.act_dtype < MOE_F32 || q.act_dtype > MOE_FP8_E4M3 || q.w_dtype < MOE_F32 ||
       q.w_dtype > MOE_FP8_E4M3)
     return MOE_ERR_INVALID_ARG;
@@ -76,6 +80,7 @@ int32_t check_problem(const moe_problem* mp, Problem* out) {
     out->topk_groups = q.n_groups > 1 ? q.topk_groups : 1;
     out->renormalize = q.renormalize; out->act = q.act_dtype; out->w = q.w_dtype;
     out->inv_tau = 1.f / tau;
+    out->capacity = q.capacity;
   }
   return MOE_OK;
 }
@@ -92,11 +97,12 @@ int64_t rows_capacity(const Problem& p) {
 
 size_t route_ws(const Problem& p) { return uses_router_gemm(p) ? align_up((size_t)p.S * p.E * 4) : 0; }
 size_t permute_ws(const Problem& p) { return align_up(permute_scratch_ints(p.S * p.K, p.E) * 4); }
+size_t capacity_ws(const Problem& p) { return align_up(capacity_scratch_ints(p.S * p.K) * 4); }
 
 // Layout of the layer workspace: consecutive 256-byte aligned regions.
 struct LayerWs {
   float* logits; int32_t* idx; float* gate; int32_t* counts; int32_t* offsets;
-  int32_t* perm; int32_t* inv; int32_t* pscratch; void* x_perm; void* h; void* y_perm;
+  int32_t* perm; int32_t* inv; int32_t* pscratch; int32_t* cscratch; void* x_perm; void* h; void* y_perm;
   float* split; size_t split_bytes;
   size_t bytes;
 };
@@ -113,6 +119,7 @@ LayerWs layer_layout(const Problem& p, char* base) {
   w.perm = (int32_t*)take((size_t)pairs * 4);
   w.inv = (int32_t*)take((size_t)pairs * 4);
   w.pscratch = (int32_t*)take(permute_scratch_ints(pairs, p.E) * 4);
+  w.cscratch = p.capacity > 0 ? (int32_t*)take(capacity_scratch_ints(pairs) * 4) : nullptr;
   w.x_perm = take((size_t)cap * p.d * act_size(p));
   w.h = take((size_t)cap * p.d_ff * act_size(p));
   w.y_perm = take((size_t)cap * p.d * act_size(p));
@@ -211,6 +218,7 @@ size_t moe_workspace_bytes(const moe_problem* mp, int32_t stage) {
     case MOE_STAGE_EXPERT_FFN: return expert_split_bytes(p) ? expert_split_bytes(p) + kAlign : 0;
     case MOE_STAGE_COMBINE: return 0;
     case MOE_STAGE_LAYER: return layer_layout(p, nullptr).bytes;
+    case MOE_STAGE_CAPACITY: return capacity_ws(p);
     default: return 0;
   }
 }
@@ -316,6 +324,21 @@ int32_t moe_load_stats(const moe_problem* mp, const int32_t* expert_counts, cons
   return hip_status(launch_load_stats(p, expert_counts, logits, dropped, alpha, stats, (hipStream_t)stream));
 }
 
+int32_t moe_apply_capacity(const moe_problem* mp, const float* logits, const float* select_bias,
+                           int32_t* topk_idx, float* topk_gate, int32_t* dropped, void* ws,
+                           size_t ws_bytes, void* stream) {
+  Problem p;
+  int32_t s = check_problem(mp, &p);
+  if (s != MOE_OK) return s;
+  if (p.S == 0) return MOE_OK;
+  for (const void* q : {(const void*)logits, (const void*)topk_idx, (const void*)topk_gate})
+    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(select_bias) || !aligned16(dropped)) return MOE_ERR_INVALID_ARG;
+  if (ws == nullptr || ws_bytes < capacity_ws(p)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_capacity(p, p.capacity, logits, select_bias, topk_idx, topk_gate, dropped,
+                                    (int32_t*)ws, (hipStream_t)stream));
+}
+
 int32_t moe_layer_forward(const moe_problem* mp, const void* x, const void* W_r,
                           const float* router_bias, const float* select_bias, const void* W1,
                           const void* b1, const void* W2, const void* b2, const float* w1_scale,
@@ -342,8 +365,14 @@ int32_t moe_layer_forward(const moe_problem* mp, const void* x, const void* W_r,
   int32_t* idx = topk_idx_out != nullptr ? topk_idx_out : w.idx;
   float* gate = topk_gate_out != nullptr ? topk_gate_out : w.gate;
   int32_t* counts = expert_counts_out != nullptr ? expert_counts_out : w.counts;
-  s = do_route(p, x, W_r, router_bias, select_bias, nullptr, logits_out, idx, gate, w.logits, st);
+  // the capacity step reads the scores again, so they are kept in that case
+  float* lg = (p.capacity > 0 && logits_out == nullptr) ? w.logits : logits_out;
+  s = do_route(p, x, W_r, router_bias, select_bias, nullptr, lg, idx, gate, w.logits, st);
   if (s != MOE_OK) return s;
+  if (p.capacity > 0) {
+    s = hip_status(launch_capacity(p, p.capacity, lg, select_bias, idx, gate, nullptr, w.cscratch, st));
+    if (s != MOE_OK) return s;
+  }
   s = hip_status(launch_permute(p, gemm_tile_m(p), idx, x, counts, w.offsets, w.perm, w.inv,
                                 w.x_perm, w.pscratch, st));
   if (s != MOE_OK) return s;

@@ -13,6 +13,7 @@ struct Problem {
   int n_groups, topk_groups, renormalize;
   int act, w;  // moe_dtype values
   float inv_tau;  // 1 / gate temperature
+  int capacity;   // per-expert limit of (token, slot) pairs, 0 = none
 };
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };

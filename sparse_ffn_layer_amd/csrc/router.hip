@@ -17,6 +17,7 @@
 // the pairwise-halving order v[j] += v[j + w], w = m/2 ... 1, over the
 // group's experts in index order.
 #include "common.h"
+#include "select.h"
 
 #include <climits>
 
@@ -26,9 +27,6 @@ constexpr int ROUTER_WAVES = 4;  // tokens per 256-thread block
 
 // Select K experts from this token's logits and write indices and gates.
 // lg[r]: unbiased logit of expert r*64 + lane (-inf where that is >= E).
-// The gates use logit / tau (inv_tau = 1 / tau; section 11.3.3's soft
-// routing temperature); at tau = 1 the product is exact, so plain gates are
-// unchanged.  Selection does not depend on tau.
 template <int R>
 __device__ __forceinline__ void select_and_gate(const float (&lg)[R], int E, int K,
                                                 const float* __restrict__ sbias, int n_groups,
@@ -37,59 +35,7 @@ __device__ __forceinline__ void select_and_gate(const float (&lg)[R], int E, int
                                                 float* __restrict__ gate_out) {
   const int lane = lane_id();
   float key[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = r * 64 + lane;
-    key[r] = lg[r];
-    if (sbias != nullptr && e < E) key[r] = lg[r] + sbias[e];
-  }
-
-  if (n_groups > 1) {
-    const int m = E / n_groups;  // power of two
-    float v[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) v[r] = key[r];
-    // pairwise-halving tree inside each group of m consecutive experts
-    for (int w = m >> 1; w >= 1; w >>= 1) {
-      if (w >= 64) {  // partner lives in register r + w/64 of the same lane
-        const int dr = w >> 6, per = m >> 6;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-          for (int s = 1; s < R; ++s) {
-            if (s == dr && r + s < R && (r % per) < dr) v[r] = v[r] + v[r + s];
-          }
-        }
-      } else {  // partner is lane + w of the same register
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float o = __shfl_down(v[r], w, 64);
-          v[r] = v[r] + o;
-        }
-      }
-    }
-    // group heads hold the scores; pick topk_groups groups
-    uint64_t chosen = 0;
-    for (int gk = 0; gk < topk_groups; ++gk) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int e = r * 64 + lane;
-        const int g = e / m;
-        if (e < E && (e % m) == 0 && !((chosen >> g) & 1ull)) {
-          if (v[r] > bv || (v[r] == bv && g < bi)) { bv = v[r]; bi = g; }
-        }
-      }
-      wave_argmax(bv, bi);
-      chosen |= 1ull << bi;
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int e = r * 64 + lane;
-      if (e < E && !((chosen >> (e / m)) & 1ull)) key[r] = -INFINITY;
-    }
-  }
+  selection_keys<R>(lg, E, sbias, n_groups, topk_groups, key);
 
   // K rounds of wave arg-max; lane k keeps slot k's expert and logit
   int my_e = 0;
@@ -115,22 +61,7 @@ __device__ __forceinline__ void select_and_gate(const float (&lg)[R], int E, int
     if (lane == k) { my_e = bi; my_l = l_sel; }
   }
 
-  float g;
-  if (renorm) {
-    const float mx = wave_max(lane < K ? my_l : -INFINITY);
-    const float ex = lane < K ? expf((my_l - mx) * inv_tau) : 0.f;
-    g = ex / wave_sum(ex);
-  } else {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < R; ++r) mx = fmaxf(mx, lg[r]);
-    mx = wave_max(mx);
-    float z = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) z += (r * 64 + lane < E) ? expf((lg[r] - mx) * inv_tau) : 0.f;
-    z = wave_sum(z);
-    g = expf((my_l - mx) * inv_tau) / z;
-  }
+  const float g = slot_gate<R>(lg, E, renorm, inv_tau, lane < K, my_l);
   if (lane < K) {
     idx_out[t * K + lane] = my_e;
     gate_out[t * K + lane] = g;

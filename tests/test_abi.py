@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -40,11 +40,12 @@ def test_struct_layout_matches_header():
 #include <stdio.h>
 #include "moe.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_problem),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_problem),
     offsetof(moe_problem, S), offsetof(moe_problem, d), offsetof(moe_problem, d_ff),
     offsetof(moe_problem, E), offsetof(moe_problem, K), offsetof(moe_problem, n_groups),
     offsetof(moe_problem, topk_groups), offsetof(moe_problem, renormalize),
-    offsetof(moe_problem, act_dtype), offsetof(moe_problem, w_dtype), offsetof(moe_problem, gate_temperature));
+    offsetof(moe_problem, act_dtype), offsetof(moe_problem, w_dtype), offsetof(moe_problem, gate_temperature),
+    offsetof(moe_problem, capacity));
   return 0;
 }'''
     with tempfile.TemporaryDirectory() as d:
@@ -69,6 +70,7 @@ def prob(**kw):
     (dict(E=0), M.MOE_ERR_INVALID_ARG),
     (dict(S=-1), M.MOE_ERR_INVALID_ARG),
     (dict(renormalize=2), M.MOE_ERR_INVALID_ARG),
+    (dict(capacity=-1), M.MOE_ERR_INVALID_ARG),
     (dict(E=12, n_groups=4, topk_groups=2), M.MOE_ERR_INVALID_ARG),   # group of 3: not a power of 2
     (dict(E=16, n_groups=3, topk_groups=1), M.MOE_ERR_INVALID_ARG),   # 16 % 3
     (dict(E=16, n_groups=4, topk_groups=0), M.MOE_ERR_INVALID_ARG),
@@ -98,6 +100,7 @@ def test_invalid_problems_rejected(kw, status):
     assert lib.moe_combine(ctypes.byref(p), *([fake] * 4), None) == status
     assert lib.moe_expert_up(ctypes.byref(p), *([fake] * 7), None, 0, None) == status
     assert lib.moe_expert_down(ctypes.byref(p), *([fake] * 7), None, 0, None) == status
+    assert lib.moe_apply_capacity(ctypes.byref(p), *([fake] * 5), fake, 1 << 40, None) == status
 
 
 @pytest.mark.parametrize("tau,ok", [(0.0, True), (1.0, True), (0.25, True), (-1.0, False),
@@ -181,3 +184,24 @@ def test_capacity_formula(S, E, K):
     cap = M.moe_rows_capacity(p)
     ws = M.moe_workspace_bytes(p, M.STAGE_LAYER)
     assert ws >= cap * (2 * 4096 + 14336) * 2
+
+
+def test_apply_capacity_argument_checks():
+    lib = M.lib()
+    p = prob(capacity=5)
+    a = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    need = M.moe_workspace_bytes(p, M.STAGE_CAPACITY)
+    assert need == 512       # S*K = 128 pair ids of 4 bytes
+    call = lambda *args: lib.moe_apply_capacity(ctypes.byref(p), *args)
+    # logits, topk_idx, topk_gate are required; select_bias and dropped are optional
+    assert call(None, None, a, a, None, a, need, None) == M.MOE_ERR_INVALID_ARG
+    assert call(a, None, None, a, None, a, need, None) == M.MOE_ERR_INVALID_ARG
+    assert call(a, None, a, None, None, a, need, None) == M.MOE_ERR_INVALID_ARG
+    assert call(a, odd, a, a, None, a, need, None) == M.MOE_ERR_INVALID_ARG
+    assert call(a, None, a, a, odd, a, need, None) == M.MOE_ERR_INVALID_ARG
+    assert call(a, None, a, a, None, a, need - 1, None) == M.MOE_ERR_WORKSPACE
+    assert call(a, None, a, a, None, None, need, None) == M.MOE_ERR_WORKSPACE
+    # a layer with a capacity needs room for the pair list on top
+    assert M.moe_workspace_bytes(p, M.STAGE_LAYER) == M.moe_workspace_bytes(prob(), M.STAGE_LAYER) + 512
+    assert lib.moe_apply_capacity(ctypes.byref(prob(S=0)), *([None] * 5), None, 0, None) == M.MOE_OK

@@ -212,3 +212,39 @@ def test_brute_force_tiny_against_exhaustive_candidate_check():
                         if pos[b] < pos[e] and b not in held:
                             assert load[b] == C
         assert (idx >= 0).sum() + dropped == S * K
+
+
+def test_layer_with_capacity_sums_kept_slots_only():
+    """The layer under a capacity: y[t] is the gate-weighted sum over the
+    token's kept slots only, computed here with torch per (token, slot); a
+    subset of tokens gives the same rows as the whole batch (the rule looks
+    at every token)."""
+    import torch
+    rng = np.random.default_rng(5)
+    S, d, d_ff, E, K, C = 24, 8, 16, 4, 2, 7
+    x = rng.standard_normal((S, d)).astype(np.float32)
+    wr = rng.standard_normal((E, d)).astype(np.float32)
+    wr[0] += 1.5 * x.mean(axis=0)                      # make expert 0 popular
+    w1 = (rng.standard_normal((E, d_ff, d)) / 3).astype(np.float32)
+    b1 = rng.standard_normal((E, d_ff)).astype(np.float32)
+    w2 = (rng.standard_normal((E, d, d_ff)) / 4).astype(np.float32)
+    b2 = rng.standard_normal((E, d)).astype(np.float32)
+    parts = O.layer_forward(x, wr, w1, b1, w2, b2, K=K, act="f32", w="f32", capacity=C, return_parts=True)
+    idx, gates = parts["idx"], parts["gates"]
+    assert (idx < 0).any() or np.bincount(idx[idx >= 0], minlength=E).max() == C
+    t64 = lambda a: torch.from_numpy(a.astype(np.float64))
+    ref = np.zeros((S, d))
+    for t in range(S):
+        for k in range(K):
+            e = idx[t, k]
+            if e >= 0:
+                h = torch.nn.functional.gelu(t64(x[t]) @ t64(w1[e]).T + t64(b1[e]), approximate="none")
+                ref[t] += gates[t, k] * (h @ t64(w2[e]).T + t64(b2[e])).numpy()
+    np.testing.assert_allclose(parts["y"], ref, rtol=1e-12, atol=1e-12)
+    sub = [0, 5, 23]
+    ys = O.layer_forward(x, wr, w1, b1, w2, b2, K=K, act="f32", w="f32", capacity=C, tokens=sub)
+    np.testing.assert_allclose(ys, parts["y"][sub], rtol=1e-13, atol=1e-13)   # fp64 BLAS order
+    # a capacity that is never reached gives the plain layer
+    y0 = O.layer_forward(x, wr, w1, b1, w2, b2, K=K, act="f32", w="f32")
+    yb = O.layer_forward(x, wr, w1, b1, w2, b2, K=K, act="f32", w="f32", capacity=S * K)
+    np.testing.assert_allclose(yb, y0, rtol=0, atol=0)
