@@ -4,11 +4,12 @@ One step = one moe_layer_forward (route, permute, expert up/down GEMMs,
 combine) over the workload's S tokens, inputs resident in HBM.  Prints ONE
 JSON line on stdout: MoE-layer tokens/s at the Mixtral-shape prefill workload
 (S=4096, d=4096, d_ff=14336, E=8, K=2, bf16), the roofline of the dominant
-kernel, the decode workload's HBM fraction, and the CPU oracle's rate on a
-bounded sample of the same workload.
+kernel, the decode workload's HBM fraction, the same layer under a
+per-expert capacity, and the CPU oracle's rate on a bounded sample of the
+same workload.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--no-decode]
+                       [--no-cpu-baseline] [--no-decode] [--no-capacity]
        python bench.py --pmc-probe [--workload NAME]     (under rocprofv3 --pmc)
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
 """
@@ -39,6 +40,7 @@ def parse():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-capacity", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only launch a 1 GiB copy and the expert GEMMs (for rocprofv3 --pmc passes)")
@@ -281,6 +283,48 @@ def run_workload(name, steps, warmup, D, M, torch):
     return cfg, w, ms, stage_ms, touched, counts
 
 
+def capacity_leg(w, M, torch, factor, steps):
+    """The workload with each expert limited to factor * S*K/E pairs: the
+    layer step with the limit, and moe_apply_capacity alone on the routed
+    indices (restored before every call, outside the timed region)."""
+    c, i = w.cfg, w.inp
+    cap = max(1, int(factor * c.S * c.K / c.E))
+    p = M.make_problem(c.S, c.d, c.d_ff, c.E, c.K, c.act, c.w, c.n_groups, c.topk_groups, c.renormalize,
+                       1.0, cap)
+    ws = M.workspace(p, M.STAGE_LAYER, "cuda")
+    counts = torch.empty(c.E, dtype=torch.int32, device="cuda")
+    logits = torch.empty((c.S, c.E), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(w.y)
+
+    def layer():
+        M.moe_layer_forward(p, i["x"], i["W_r"], i["W1"], i["b1"], i["W2"], i["b2"], i["router_bias"],
+                            i["select_bias"], i["w1_scale"], i["w2_scale"], y=y, expert_counts_out=counts,
+                            logits_out=logits, ws=ws)
+
+    layer_ms = time_calls(torch, layer, steps, 3)
+    M.moe_route(w.p, i["x"], i["W_r"], i["router_bias"], i["select_bias"], topk_idx=w.idx, topk_gate=w.gate,
+                ws=w.ws_route)
+    idx0 = w.idx.clone()
+    ws_c = M.workspace(p, M.STAGE_CAPACITY, "cuda")
+    dropped = torch.zeros(4, dtype=torch.int32, device="cuda")
+    evs = []
+    for k in range(steps + 3):
+        w.idx.copy_(idx0)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        M.moe_apply_capacity(p, logits, w.idx, i["select_bias"], w.gate, dropped, ws=ws_c)
+        e.record()
+        if k >= 3:
+            evs.append((s, e))
+    torch.cuda.synchronize()
+    apply_ms = sum(s.elapsed_time(e) for s, e in evs) / len(evs)
+    nd = int(dropped.cpu()[0])
+    moved = int((w.idx != idx0).sum().cpu()) - nd
+    return {"factor": factor, "capacity": cap, "layer_ms_per_step": round(layer_ms, 4),
+            "tokens_per_s": round(c.S / (layer_ms / 1e3), 1), "apply_capacity_ms": round(apply_ms, 4),
+            "rerouted_pairs": moved, "dropped_pairs": nd, "drop_rate": round(nd / (c.S * c.K), 5)}
+
+
 def cpu_baseline(cfg, w, target_s, torch):
     """The oracle, as it is, on the first n tokens of the same workload."""
     import numpy as np
@@ -363,6 +407,9 @@ def main():
         "layer_tflops": round(4.0 * cfg.S * cfg.K * cfg.d * cfg.d_ff / (ms / 1e3) / 1e12, 2),
     }
     log(f"[bench] {cfg.name}: {ms:.3f} ms/step, stages {out['stage_ms']}")
+    if not a.no_capacity:
+        out["capacity"] = capacity_leg(w, M, torch, 1.25, a.steps)
+        log(f"[bench] capacity: {out['capacity']}")
     if not a.no_decode and cfg.name != "decode":
         dcfg, dw, dms, dstage, dtouched, _ = run_workload("decode", max(a.steps, 100), a.warmup, D, M, torch)
         out["decode"] = {"workload": "decode", "tokens_per_s": round(dcfg.S / (dms / 1e3), 1),

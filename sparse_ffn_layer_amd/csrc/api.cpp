@@ -34,7 +34,7 @@ hipError_t launch_load_stats(const Problem&, const int32_t*, const float*, const
                              float*, hipStream_t);
 hipError_t launch_capacity(const Problem&, int, const float*, const float*, int32_t*, float*,
                            int32_t*, int32_t*, hipStream_t);
-size_t capacity_scratch_ints(int64_t pairs);
+size_t capacity_scratch_ints(int64_t pairs, int E);
 int gemm_tile_m(const Problem& p);
 }  // namespace sfl
 
@@ -97,7 +97,7 @@ int64_t rows_capacity(const Problem& p) {
 
 size_t route_ws(const Problem& p) { return uses_router_gemm(p) ? align_up((size_t)p.S * p.E * 4) : 0; }
 size_t permute_ws(const Problem& p) { return align_up(permute_scratch_ints(p.S * p.K, p.E) * 4); }
-size_t capacity_ws(const Problem& p) { return align_up(capacity_scratch_ints(p.S * p.K) * 4); }
+size_t capacity_ws(const Problem& p) { return align_up(capacity_scratch_ints(p.S * p.K, p.E) * 4); }
 
 // Layout of the layer workspace: consecutive 256-byte aligned regions.
 struct LayerWs {
@@ -119,7 +119,7 @@ LayerWs layer_layout(const Problem& p, char* base) {
   w.perm = (int32_t*)take((size_t)pairs * 4);
   w.inv = (int32_t*)take((size_t)pairs * 4);
   w.pscratch = (int32_t*)take(permute_scratch_ints(pairs, p.E) * 4);
-  w.cscratch = p.capacity > 0 ? (int32_t*)take(capacity_scratch_ints(pairs) * 4) : nullptr;
+  w.cscratch = p.capacity > 0 ? (int32_t*)take(capacity_scratch_ints(pairs, p.E) * 4) : nullptr;
   w.x_perm = take((size_t)cap * p.d * act_size(p));
   w.h = take((size_t)cap * p.d_ff * act_size(p));
   w.y_perm = take((size_t)cap * p.d * act_size(p));

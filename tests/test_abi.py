@@ -192,7 +192,7 @@ def test_apply_capacity_argument_checks():
     a = ctypes.c_void_p(1 << 20)
     odd = ctypes.c_void_p((1 << 20) + 4)
     need = M.moe_workspace_bytes(p, M.STAGE_CAPACITY)
-    assert need == 512       # S*K = 128 pair ids of 4 bytes
+    assert need == ((64 * 2 + 4 + 8) * 4 + 255) // 256 * 256   # pair list, 4 state ints, run[E]
     call = lambda *args: lib.moe_apply_capacity(ctypes.byref(p), *args)
     # logits, topk_idx, topk_gate are required; select_bias and dropped are optional
     assert call(None, None, a, a, None, a, need, None) == M.MOE_ERR_INVALID_ARG
@@ -203,5 +203,5 @@ def test_apply_capacity_argument_checks():
     assert call(a, None, a, a, None, a, need - 1, None) == M.MOE_ERR_WORKSPACE
     assert call(a, None, a, a, None, None, need, None) == M.MOE_ERR_WORKSPACE
     # a layer with a capacity needs room for the pair list on top
-    assert M.moe_workspace_bytes(p, M.STAGE_LAYER) == M.moe_workspace_bytes(prob(), M.STAGE_LAYER) + 512
+    assert M.moe_workspace_bytes(p, M.STAGE_LAYER) == M.moe_workspace_bytes(prob(), M.STAGE_LAYER) + need
     assert lib.moe_apply_capacity(ctypes.byref(prob(S=0)), *([None] * 5), None, 0, None) == M.MOE_OK
