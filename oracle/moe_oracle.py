@@ -52,6 +52,7 @@ __all__ = [
     "router_logits", "softmax", "group_scores_f32", "select_experts",
     "gate_weights", "permute", "gelu", "expert_ffn", "layer_forward",
     "combine", "load_stats", "STAT_NAMES", "selection_keys", "apply_capacity",
+    "E4M3_MAX", "encode_e4m3fn", "quantize_rows_e4m3", "dequantize_rows_e4m3", "expert_ffn_w8a8",
 ]
 
 
@@ -90,6 +91,55 @@ def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
     """e4m3fn codes (uint8) -> float64 by the definition above, evaluated
     once for all 256 codes and looked up."""
     return _E4M3FN_TABLE[np.asarray(codes).astype(np.uint8)]
+
+
+E4M3_MAX = 448.0
+
+
+def encode_e4m3fn(v: np.ndarray) -> np.ndarray:
+    """float32 values with |v| <= 448 -> the nearest e4m3fn code (uint8),
+    ties to the even code (the code's last bit is the mantissa's last bit,
+    and codes of one sign are ordered by magnitude).  The sign bit follows
+    the sign of v, so -0.0 and small negatives that round to zero give 0x80.
+    Written from the format's definition (decode_e4m3fn) by a nearest-value
+    search over the 127 finite non-negative codes."""
+    v = np.asarray(v, dtype=np.float32)
+    if np.any(~np.isfinite(v)) or np.any(np.abs(v) > E4M3_MAX):
+        raise ValueError("encode_e4m3fn takes finite values with |v| <= 448")
+    mags = _E4M3FN_TABLE[:0x7F]                      # codes 0x00..0x7E, increasing
+    a = np.abs(v).astype(np.float64)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def quantize_rows_e4m3(v: np.ndarray):
+    """Per-row fp8 quantisation of activations: for each row, scale s =
+    amax / 448 (amax the largest |v| of the row; one float32 division) and
+    code q = encode(clip(v / s, -448, 448)) with v / s one float32 division;
+    the row's value is decode(q) * s.  A row of zeros gets s = 0 and codes 0.
+    FP8 E4M3 is the format the pages recommend for expert weights ([P1]
+    section 3.3); applying it to the activations with a per-row (per-token)
+    scale is the W8A8 reading, so that both GEMM operands are fp8.
+    v: float32 [R, n].  Returns (codes uint8 [R, n], scales float32 [R])."""
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.abs(v).max(axis=1) if v.shape[1] else np.zeros(v.shape[0], np.float32)
+    s = (amax.astype(np.float32) / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    t = (v / safe[:, None]).astype(np.float32)
+    t = np.clip(t, np.float32(-E4M3_MAX), np.float32(E4M3_MAX)).astype(np.float32)
+    codes = encode_e4m3fn(t)
+    codes[s == 0] = 0
+    return codes, s
+
+
+def dequantize_rows_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """decode(q) * s per row, float64 (exact: a 4-bit significand times a
+    float32)."""
+    return decode_e4m3fn(codes) * np.asarray(scales, dtype=np.float32).astype(np.float64)[:, None]
 
 
 def decode(arr: np.ndarray, dtype: str) -> np.ndarray:
@@ -393,6 +443,23 @@ def expert_ffn(x_rows: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarra
     return (h, o) if return_hidden else o
 
 
+def expert_ffn_w8a8(x_rows: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray,
+                    b2: np.ndarray, return_hidden: bool = False):
+    """The expert FFN with fp8 activations (W8A8): the rows entering each
+    product are quantised per row (quantize_rows_e4m3) first.
+      x -> (qx, sx);  h = GeLU(dequant(qx, sx) W1 + b1);
+      h -> (qh, sh);  out = dequant(qh, sh) W2 + b2.
+    x_rows float64 holding float32 values (bf16 activations are exact); h is
+    quantised from its float32 rounding.  Weights as in expert_ffn (float64,
+    fp8 weights already times their channel scale)."""
+    qx, sx = quantize_rows_e4m3(x_rows.astype(np.float32))
+    a = dequantize_rows_e4m3(qx, sx) @ w1.T + b1[None, :]
+    h = gelu(a)
+    qh, sh = quantize_rows_e4m3(h.astype(np.float32))
+    o = dequantize_rows_e4m3(qh, sh) @ w2.T + b2[None, :]
+    return (h, o) if return_hidden else o
+
+
 def combine(gates: np.ndarray, outputs: np.ndarray) -> np.ndarray:
     """y[t] = sum_k gate[t,k] * E_{idx[t,k]}(x_t) ([P2] 11.1.1 weighted sum;
     [P3] one MoE forward: outputs weighted by score and summed).
@@ -405,7 +472,7 @@ def layer_forward(x: np.ndarray, w_r: np.ndarray, W1, b1, W2, b2, *, K: int,
                   n_groups: int = 1, topk_groups: int = 1, renormalize: int = 1,
                   temperature: float = 1.0, w1_scale=None, w2_scale=None, logits_in=None,
                   tokens: Optional[Sequence[int]] = None, capacity: int = 0,
-                  return_parts: bool = False):
+                  act_quant: bool = False, return_parts: bool = False):
     """The whole layer for the tokens `tokens` (default: all), [P2] 11.1.1-2.
 
     x [S,d] and w_r [E,d] are storage arrays of dtype `act`; W1 [E][d_ff,d],
@@ -413,6 +480,7 @@ def layer_forward(x: np.ndarray, w_r: np.ndarray, W1, b1, W2, b2, *, K: int,
     only the experts in use are read); b1 [E][d_ff], b2 [E][d] of dtype
     `act`; w1_scale [E][d_ff], w2_scale [E][d] float32 for fp8 weights.
     logits_in [S,E] float32 replaces the router product when given.
+    act_quant: fp8 activations in both expert products (expert_ffn_w8a8).
     capacity > 0 limits each expert to that many (token, slot) pairs with
     apply_capacity; that rule looks at every token, so the routing is then
     computed for all S tokens before `tokens` are picked.
@@ -450,8 +518,8 @@ def layer_forward(x: np.ndarray, w_r: np.ndarray, W1, b1, W2, b2, *, K: int,
         s2 = None if w2_scale is None else w2_scale[e]
         W1e = expert_matrix(W1[e], w, s1)
         W2e = expert_matrix(W2[e], w, s2)
-        h, o = expert_ffn(xs[rows], W1e, decode(b1[e], act), W2e, decode(b2[e], act),
-                          return_hidden=True)
+        ffn = expert_ffn_w8a8 if act_quant else expert_ffn
+        h, o = ffn(xs[rows], W1e, decode(b1[e], act), W2e, decode(b2[e], act), return_hidden=True)
         outs[rows, slots] = o
         if return_parts:
             hidden[int(e)] = (rows, slots, h)
