@@ -117,19 +117,21 @@ def encode_e4m3fn(v: np.ndarray) -> np.ndarray:
 
 
 def quantize_rows_e4m3(v: np.ndarray):
-    """Per-row fp8 quantisation of activations: for each row, scale s =
-    amax / 448 (amax the largest |v| of the row; one float32 division) and
-    code q = encode(clip(v / s, -448, 448)) with v / s one float32 division;
-    the row's value is decode(q) * s.  A row of zeros gets s = 0 and codes 0.
+    """Per-row fp8 quantisation of activations: for each row with amax the
+    largest |v|, the scale is s = amax / 448 and the codes are q =
+    encode(clip(v * r, -448, 448)) with r = 448 / amax (each quotient and
+    the product one float32 operation); the row's value is decode(q) * s.
+    A row of zeros gets s = 0 and codes 0.
     FP8 E4M3 is the format the pages recommend for expert weights ([P1]
     section 3.3); applying it to the activations with a per-row (per-token)
     scale is the W8A8 reading, so that both GEMM operands are fp8.
     v: float32 [R, n].  Returns (codes uint8 [R, n], scales float32 [R])."""
     v = np.asarray(v, dtype=np.float32)
     amax = np.abs(v).max(axis=1) if v.shape[1] else np.zeros(v.shape[0], np.float32)
-    s = (amax.astype(np.float32) / np.float32(E4M3_MAX)).astype(np.float32)
-    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
-    t = (v / safe[:, None]).astype(np.float32)
+    amax = amax.astype(np.float32)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    r = (np.float32(E4M3_MAX) / np.where(amax > 0, amax, np.float32(1.0))).astype(np.float32)
+    t = (v * r[:, None]).astype(np.float32)
     t = np.clip(t, np.float32(-E4M3_MAX), np.float32(E4M3_MAX)).astype(np.float32)
     codes = encode_e4m3fn(t)
     codes[s == 0] = 0

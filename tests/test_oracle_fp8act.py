@@ -83,7 +83,8 @@ def test_quantize_rows_against_torch_conversion():
     q, s = O.quantize_rows_e4m3(v)
     t = torch.from_numpy(v)
     st = t.abs().amax(dim=1) / 448.0
-    qt = (t / st[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    rt = 448.0 / t.abs().amax(dim=1)
+    qt = (t * rt[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     np.testing.assert_array_equal(s, st.numpy())
     np.testing.assert_array_equal(q, qt)
 
@@ -119,7 +120,7 @@ def test_w8a8_expert_against_loops_with_torch_quantiser():
     def tq(row):
         t = torch.from_numpy(np.asarray(row, np.float32))
         sc = t.abs().max() / 448.0
-        q = (t / sc).clamp(-448, 448).to(torch.float8_e4m3fn).to(torch.float64)
+        q = (t * (448.0 / t.abs().max())).clamp(-448, 448).to(torch.float8_e4m3fn).to(torch.float64)
         return (q * sc.double()).numpy()
 
     y = O.expert_ffn_w8a8(x.astype(np.float64), w1, b1, w2, b2)
