@@ -91,6 +91,14 @@ typedef enum {
  *  - capacity: the most (token, slot) pairs one expert takes in
  *    moe_layer_forward and moe_apply_capacity (chapter 11 section 11.3.3,
  *    expert dropping); 0 = no limit; negative: MOE_ERR_INVALID_ARG.
+ *  - act_quant: 1 = fp8 activations (W8A8) in moe_layer_forward: the rows
+ *    entering each expert product (x, then h) are quantised per row as
+ *    moe_quantize_rows does, and both products run on fp8 MFMAs; the result
+ *    is dequantised by row scale times weight channel scale.  Needs
+ *    act_dtype BF16, w_dtype FP8_E4M3, d and d_ff multiples of 128 (else
+ *    MOE_ERR_UNSUPPORTED).  moe_permute and the expert entry points take
+ *    bf16 activations and return MOE_ERR_UNSUPPORTED when it is set.
+ *    0 = activations in act_dtype; other values: MOE_ERR_INVALID_ARG.
  *  - Limits: 1 <= E <= 512, 1 <= K <= min(E, 64), d and d_ff multiples of 64,
  *    S < 2^31 / K.  Outside them: MOE_ERR_UNSUPPORTED. */
 typedef struct {
@@ -106,6 +114,7 @@ typedef struct {
   int32_t w_dtype;   /* moe_dtype */
   float gate_temperature;
   int32_t capacity;
+  int32_t act_quant;
 } moe_problem;
 
 /* Host-only, pure helpers (no HIP call).  They return 0 / -1 for a problem
@@ -240,6 +249,20 @@ enum {
 };
 int32_t moe_load_stats(const moe_problem* p, const int32_t* expert_counts, const float* logits,
                        const int32_t* dropped, float alpha, float* stats, void* stream);
+
+/* Per-row fp8 quantisation of bf16 activations ("MoE 推理工程深层实战"
+ * section 3.3: FP8 E4M3 is the production format for experts; here it is
+ * applied to the activations of the W8A8 expert products).  For each row r
+ * of src [rows][n] (bf16), with amax the largest |value| of the row:
+ *     scales[r] = amax / 448,   codes[r][i] = e4m3(clamp(v * (448 / amax),
+ *     -448, 448)), round to nearest even (OCP E4M3FN codes),
+ * each quotient and product one float32 operation; the row's value is
+ * decode(code) * scale.  A row of zeros gets scale 0 and codes 0.
+ *   codes [rows][n] uint8 and scales [rows] float32 are written.
+ *   n: a positive multiple of 8; rows >= 0 (0 is a no-op), < 2^31.
+ * Needs no workspace and no moe_problem. */
+int32_t moe_quantize_rows(const void* src, int64_t rows, int32_t n, uint8_t* codes, float* scales,
+                          void* stream);
 
 /* Capacity-limited dispatch (chapter 11 section 11.3.3, expert dropping:
  * the excess of an overloaded expert moves to the next-best expert;

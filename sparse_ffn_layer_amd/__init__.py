@@ -18,7 +18,7 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "STAGE_ROUTE", "STAGE_PERMUTE", "STAGE_EXPERT_FFN",
     "STAGE_COMBINE", "STAGE_LAYER", "MoEError", "moe_problem", "make_problem", "lib", "LIB_PATH",
     "moe_workspace_bytes", "moe_tile_m", "moe_rows_capacity", "moe_status_string",
-    "workspace", "moe_load_stats", "moe_apply_capacity", "STAGE_CAPACITY", "MOE_STATS_N", "STAT_NAMES", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
+    "workspace", "moe_load_stats", "moe_apply_capacity", "moe_quantize_rows", "STAGE_CAPACITY", "MOE_STATS_N", "STAT_NAMES", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfl_moe.so")
@@ -46,13 +46,14 @@ class moe_problem(ctypes.Structure):
                 ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("topk_groups", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
-                ("gate_temperature", ctypes.c_float), ("capacity", ctypes.c_int32)]
+                ("gate_temperature", ctypes.c_float), ("capacity", ctypes.c_int32),
+                ("act_quant", ctypes.c_int32)]
 
 
 def make_problem(S, d, d_ff, E, K, act="bf16", w="bf16", n_groups=1, topk_groups=1,
-                 renormalize=1, temperature=1.0, capacity=0) -> moe_problem:
+                 renormalize=1, temperature=1.0, capacity=0, act_quant=0) -> moe_problem:
     return moe_problem(int(S), int(d), int(d_ff), int(E), int(K), int(n_groups), int(topk_groups),
-                       int(renormalize), _DT[act], _DT[w], float(temperature), int(capacity))
+                       int(renormalize), _DT[act], _DT[w], float(temperature), int(capacity), int(act_quant))
 
 
 _lib = None
@@ -73,6 +74,7 @@ _SIGS = {
     "moe_layer_forward": (_i32, [_P] + [_vp] * 15 + [_vp, _sz, _vp]),
     "moe_load_stats": (_i32, [_P, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "moe_apply_capacity": (_i32, [_P] + [_vp] * 5 + [_vp, _sz, _vp]),
+    "moe_quantize_rows": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
 }
 
 
@@ -264,3 +266,16 @@ def moe_apply_capacity(p, logits, topk_idx, select_bias=None, topk_gate=None, dr
                                   _ptr(topk_gate), _ptr(dropped), _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_apply_capacity", st)
     return topk_idx, topk_gate, dropped[:1]
+
+
+def moe_quantize_rows(src, codes=None, scales=None, stream=None):
+    """Per-row e4m3 quantisation of a bf16 matrix [rows, n]: returns (codes
+    uint8 [rows, n], scales float32 [rows])."""
+    rows, n = src.shape
+    if codes is None:
+        codes = torch.empty((rows, n), dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty(max(rows, 1), dtype=torch.float32, device=src.device)
+    st = lib().moe_quantize_rows(_ptr(src), int(rows), int(n), _ptr(codes), _ptr(scales), _stream(stream))
+    _check("moe_quantize_rows", st)
+    return codes, scales[:rows]

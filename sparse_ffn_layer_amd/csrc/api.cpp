@@ -11,7 +11,7 @@
 #include "common.h"
 
 namespace sfl {
-// kernels (router.hip, capacity.hip, permute.hip, gemm.hip, combine.hip)
+// kernels (router.hip, capacity.hip, permute.hip, quant.hip, gemm.hip, combine.hip)
 hipError_t launch_router_fused(const Problem&, const void*, const void*, const float*,
                                const float*, float*, int32_t*, float*, hipStream_t);
 hipError_t launch_route_logits(const Problem&, const float*, const float*, float*, int32_t*,
@@ -23,10 +23,12 @@ hipError_t launch_permute(const Problem&, int, const int32_t*, const void*, int3
 size_t permute_scratch_ints(int64_t pairs, int E);
 hipError_t launch_expert_up(const Problem&, int64_t, const void*, const int32_t*, const int32_t*,
                             const void*, const void*, const float*, void*, float*, size_t,
-                            hipStream_t);
+                            hipStream_t, const float*);
 hipError_t launch_expert_down(const Problem&, int64_t, const void*, const int32_t*,
                               const int32_t*, const void*, const void*, const float*, void*,
-                              float*, size_t, hipStream_t);
+                              float*, size_t, hipStream_t, const float*);
+hipError_t launch_quantize_rows(const uint16_t*, int64_t, int, int64_t, int, bool, const int32_t*,
+                                uint8_t*, int64_t, float*, hipStream_t);
 size_t expert_split_bytes(const Problem& p);
 hipError_t launch_combine(const Problem&, const void*, const int32_t*, const float*, void*,
                           hipStream_t);
@@ -58,6 +60,7 @@ int32_t check_problem(const moe_problem* mp, Problem* out) {
   const float tau = q.gate_temperature == 0.f ? 1.f : q.gate_temperature;
   if (!(tau > 0.f) || !(tau < INFINITY)) return MOE_ERR_INVALID_ARG;
   if (q.capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (q.act_quant != 0 && q.act_quant != 1) return MOE_ERR_INVALID_ARG;
   if (q.act_dtype < MOE_F32 || q.act_dtype > MOE_FP8_E4M3 || q.w_dtype < MOE_F32 ||
       q.w_dtype > MOE_FP8_E4M3)
     return MOE_ERR_INVALID_ARG;
@@ -74,6 +77,10 @@ int32_t check_problem(const moe_problem* mp, Problem* out) {
   if (!combo) return MOE_ERR_UNSUPPORTED;
   if (q.E > 512 || q.K > 64 || q.d % 64 != 0 || q.d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (q.S > 0 && q.S >= (int64_t)(INT32_MAX / 2) / q.K) return MOE_ERR_UNSUPPORTED;
+  // fp8 activations: bf16 activations and fp8 weights, k a multiple of 128
+  if (q.act_quant && (q.act_dtype != MOE_BF16 || q.w_dtype != MOE_FP8_E4M3 || q.d % 128 != 0 ||
+                      q.d_ff % 128 != 0))
+    return MOE_ERR_UNSUPPORTED;
   if (out != nullptr) {
     out->S = q.S; out->d = q.d; out->d_ff = q.d_ff; out->E = q.E; out->K = q.K;
     out->n_groups = q.n_groups > 1 ? q.n_groups : 1;
@@ -81,6 +88,7 @@ int32_t check_problem(const moe_problem* mp, Problem* out) {
     out->renormalize = q.renormalize; out->act = q.act_dtype; out->w = q.w_dtype;
     out->inv_tau = 1.f / tau;
     out->capacity = q.capacity;
+    out->act_quant = q.act_quant;
   }
   return MOE_OK;
 }
@@ -103,6 +111,7 @@ size_t capacity_ws(const Problem& p) { return align_up(capacity_scratch_ints(p.S
 struct LayerWs {
   float* logits; int32_t* idx; float* gate; int32_t* counts; int32_t* offsets;
   int32_t* perm; int32_t* inv; int32_t* pscratch; int32_t* cscratch; void* x_perm; void* h; void* y_perm;
+  uint8_t* h8; float* xs; float* hs;  // fp8 activations: h codes, row scales of x_perm and h
   float* split; size_t split_bytes;
   size_t bytes;
 };
@@ -123,6 +132,11 @@ LayerWs layer_layout(const Problem& p, char* base) {
   w.x_perm = take((size_t)cap * p.d * act_size(p));
   w.h = take((size_t)cap * p.d_ff * act_size(p));
   w.y_perm = take((size_t)cap * p.d * act_size(p));
+  if (p.act_quant) {  // x_perm then holds the e4m3 codes of x (fewer bytes than bf16)
+    w.h8 = (uint8_t*)take((size_t)cap * p.d_ff);
+    w.xs = (float*)take((size_t)cap * 4);
+    w.hs = (float*)take((size_t)cap * 4);
+  }
   w.split_bytes = expert_split_bytes(p);
   w.split = (float*)take(w.split_bytes);
   w.bytes = off;
@@ -139,10 +153,10 @@ int32_t do_expert_ffn(const Problem& p, const void* x_perm, const int32_t* count
   const bool fp8 = p.w == DT_FP8;
   const int64_t cap = rows_capacity(p);
   int32_t s = hip_status(launch_expert_up(p, cap, x_perm, counts, offsets, W1, b1, fp8 ? s1 : nullptr,
-                                          h, split, split_bytes, st));
+                                          h, split, split_bytes, st, nullptr));
   if (s != MOE_OK) return s;
   return hip_status(launch_expert_down(p, cap, h, counts, offsets, W2, b2, fp8 ? s2 : nullptr,
-                                       y_perm, split, split_bytes, st));
+                                       y_perm, split, split_bytes, st, nullptr));
 }
 
 // The split-K workspace inside a caller's buffer (aligned start), or null.
@@ -160,7 +174,9 @@ float* split_region(void* ws, size_t ws_bytes, size_t* usable) {
 int32_t check_expert(const moe_problem* mp, Problem* p, std::initializer_list<const void*> req,
                      const float* scale) {
   int32_t s = check_problem(mp, p);
-  if (s != MOE_OK || p->S == 0) return s;
+  if (s != MOE_OK) return s;
+  if (p->act_quant) return MOE_ERR_UNSUPPORTED;  // fp8 activations: moe_layer_forward only
+  if (p->S == 0) return s;
   for (const void* q : req)
     if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
   if (p->w == DT_FP8 && scale == nullptr) return MOE_ERR_INVALID_ARG;
@@ -247,6 +263,7 @@ int32_t moe_permute(const moe_problem* mp, const int32_t* topk_idx, const void* 
   Problem p;
   int32_t s = check_problem(mp, &p);
   if (s != MOE_OK) return s;
+  if (p.act_quant) return MOE_ERR_UNSUPPORTED;  // fp8 activations: moe_layer_forward only
   if (p.S == 0) return MOE_OK;
   const void* ptrs[] = {topk_idx, x, expert_counts, expert_offsets, perm, inv_perm, x_perm};
   for (const void* q : ptrs)
@@ -283,7 +300,7 @@ int32_t moe_expert_up(const moe_problem* mp, const void* x_perm, const int32_t* 
   float* split = split_region(ws, ws_bytes, &usable);
   return hip_status(launch_expert_up(p, rows_capacity(p), x_perm, expert_counts, expert_offsets, W1,
                                      b1, p.w == DT_FP8 ? w1_scale : nullptr, h, split, usable,
-                                     (hipStream_t)stream));
+                                     (hipStream_t)stream, nullptr));
 }
 
 int32_t moe_expert_down(const moe_problem* mp, const void* h, const int32_t* expert_counts,
@@ -296,7 +313,7 @@ int32_t moe_expert_down(const moe_problem* mp, const void* h, const int32_t* exp
   float* split = split_region(ws, ws_bytes, &usable);
   return hip_status(launch_expert_down(p, rows_capacity(p), h, expert_counts, expert_offsets, W2, b2,
                                        p.w == DT_FP8 ? w2_scale : nullptr, y_perm, split, usable,
-                                       (hipStream_t)stream));
+                                       (hipStream_t)stream, nullptr));
 }
 
 int32_t moe_combine(const moe_problem* mp, const void* y_perm, const int32_t* inv_perm,
@@ -322,6 +339,17 @@ int32_t moe_load_stats(const moe_problem* mp, const int32_t* expert_counts, cons
   for (const void* q : {(const void*)expert_counts, (const void*)logits, (const void*)dropped, (const void*)stats})
     if (q != nullptr && !aligned16(q)) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_load_stats(p, expert_counts, logits, dropped, alpha, stats, (hipStream_t)stream));
+}
+
+int32_t moe_quantize_rows(const void* src, int64_t rows, int32_t n, uint8_t* codes, float* scales,
+                          void* stream) {
+  if (rows < 0 || n < 8 || n % 8 != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (rows > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  for (const void* q : {(const void*)src, (const void*)codes, (const void*)scales})
+    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_rows((const uint16_t*)src, n, n, rows, 1, false, nullptr, codes, n, scales,
+                                         (hipStream_t)stream));
 }
 
 int32_t moe_apply_capacity(const moe_problem* mp, const float* logits, const float* select_bias,
@@ -372,6 +400,27 @@ int32_t moe_layer_forward(const moe_problem* mp, const void* x, const void* W_r,
   if (p.capacity > 0) {
     s = hip_status(launch_capacity(p, p.capacity, lg, select_bias, idx, gate, nullptr, w.cscratch, st));
     if (s != MOE_OK) return s;
+  }
+  if (p.act_quant) {
+    // W8A8: the gather writes e4m3 rows and row scales; h is quantised per
+    // row between the two products
+    const int64_t pairs = p.S * p.K, cap = rows_capacity(p);
+    uint8_t* x8 = (uint8_t*)w.x_perm;
+    s = hip_status(launch_permute(p, gemm_tile_m(p), idx, x, counts, w.offsets, w.perm, w.inv, nullptr,
+                                  w.pscratch, st));
+    if (s != MOE_OK) return s;
+    s = hip_status(launch_quantize_rows((const uint16_t*)x, p.d, p.d, pairs, p.K, true, w.inv, x8, p.d, w.xs, st));
+    if (s != MOE_OK) return s;
+    s = hip_status(launch_expert_up(p, cap, x8, counts, w.offsets, W1, b1, w1_scale, w.h, w.split,
+                                    w.split_bytes, st, w.xs));
+    if (s != MOE_OK) return s;
+    s = hip_status(launch_quantize_rows((const uint16_t*)w.h, p.d_ff, p.d_ff, pairs, p.K, false, w.inv, w.h8,
+                                        p.d_ff, w.hs, st));
+    if (s != MOE_OK) return s;
+    s = hip_status(launch_expert_down(p, cap, w.h8, counts, w.offsets, W2, b2, w2_scale, w.y_perm, w.split,
+                                      w.split_bytes, st, w.hs));
+    if (s != MOE_OK) return s;
+    return hip_status(launch_combine(p, w.y_perm, w.inv, gate, y, st));
   }
   s = hip_status(launch_permute(p, gemm_tile_m(p), idx, x, counts, w.offsets, w.perm, w.inv,
                                 w.x_perm, w.pscratch, st));

@@ -14,6 +14,7 @@ struct Problem {
   int act, w;  // moe_dtype values
   float inv_tau;  // 1 / gate temperature
   int capacity;   // per-expert limit of (token, slot) pairs, 0 = none
+  int act_quant;  // 1: e4m3 activations with per-row scales in the expert products
 };
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
@@ -25,6 +26,7 @@ inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);

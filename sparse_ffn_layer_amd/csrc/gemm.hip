@@ -9,10 +9,14 @@
 // batch through one expert turns many small products into one large GEMM.
 //
 // out[r][n] = epilogue( sum_k A[r][k] * B_g[n][k] )  for the rows r of group g
-//   A    : activations, bf16, row-major [rows][K]
+//   A    : activations, bf16, row-major [rows][K]; or (W8A8) OCP e4m3
+//          codes with one float32 scale per row
 //   B_g  : weights of group g in linear-layer layout [N][K] (bf16 or OCP
-//          e4m3 fp8, converted exactly to bf16 on the way into the MFMAs)
-//   epilogue: * scale_g[n] (fp8), + bias_g[n], optional exact GeLU, round
+//          e4m3 fp8; with bf16 activations the codes are converted exactly
+//          to bf16 on the way into the MFMAs, with e4m3 activations both
+//          operands go to the fp8 MFMAs)
+//   epilogue: * scale_g[n] (fp8) * row scale (W8A8), + bias_g[n], optional
+//          exact GeLU, round
 //
 // Rows of group g occupy [offsets[g], offsets[g] + counts[g]) and every
 // group starts at a multiple of the row tile, so a BM x BN tile never
@@ -52,6 +56,7 @@ struct GemmArgs {
   int64_t ldb;       // elements
   int64_t b_gstride;  // elements between consecutive groups
   const float* scale;  // [G][N] fp8 channel scales or null
+  const float* a_scale;  // [rows] scale of each e4m3 activation row (W8A8) or null
   const void* bias;    // [G][N] (bf16 for EPI_GELU/EPI_BIAS, f32 for EPI_F32) or null
   void* C;
   int64_t ldc;
@@ -170,7 +175,7 @@ __device__ __forceinline__ float acc_get(const acc_t& v, int k) {
 }
 
 template <int BN, int WM, int WN, bool BFP8, int EPI, int MF, int FM, int FN, int NACC, bool AREAD = false,
-          typename acc_t>
+          bool A8 = false, typename acc_t>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const acc_t (&acc)[FM][FN], int g, int rows,
                                               int64_t row0, int n0, int wm, int wn, int lr, int lk) {
   constexpr int WTN = BN / WN;
@@ -206,11 +211,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const acc_t (&a
         if (wm * WTM + i * MF >= rows) continue;  // uniform: fragment wholly past the rows
         const int m = wm * WTM + i * MF + lr;
         if (m < rows) {
+          const float rs = A8 ? a.a_scale[row0 + m] : 1.f;
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float x = acc_get<AREAD>(acc[i][j], q4 * 4 + q);
             float t = BFP8 ? x * sc[q] : x;
+            if constexpr (A8) t *= rs;
             t += bi[q];
             if constexpr (EPI == EPI_GELU) t = gelu_erf(t);
             v[q] = t;
@@ -232,14 +239,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const acc_t (&a
 // fragment, 8 consecutive k values starting at 8 * (lane / MF).  Result
 // lanes (weights as the first operand): activation row m = lane % MF, four
 // consecutive output channels n per group of four accumulator registers.
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF>
+// A8 (e4m3 activations, requires BFP8): the fp8 MFMAs
+// v_mfma_f32_{16x16x128,32x32x64}_f8f6f4 (issued through the block-scaled
+// form with unit scales); each lane supplies 32 codes of its row for both
+// operands, taken from the same k positions, so the products pair up
+// whatever order the hardware reads the 32 bytes in.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF, bool A8 = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_bf16_kernel(const GemmArgs a) {
+  static_assert(!A8 || BFP8, "e4m3 activations go with e4m3 weights");
   constexpr int NT = 64 * WM * WN;
   constexpr int BSZ = BFP8 ? 1 : 2;
-  constexpr int CA = BK * 2 / 16;    // 16-byte chunks per A row
+  constexpr int ASZ = A8 ? 1 : 2;
+  constexpr bool PAIR = BFP8 && !A8;  // fp8 weights widened to bf16: k-steps in pairs
+  constexpr int CA = BK * ASZ / 16;  // 16-byte chunks per A row
   constexpr int CB = BK * BSZ / 16;  // 16-byte chunks per B row
-  constexpr int A_BYTES = BM * BK * 2;
+  constexpr int A_BYTES = BM * BK * ASZ;
   constexpr int B_BYTES = BN * BK * BSZ;
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int A_LOADS = BM * CA / NT;
@@ -247,13 +262,17 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   constexpr int LOADS = A_LOADS + B_LOADS;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / MF, FN = WTN / MF;
-  constexpr int KSTEP = MF == 16 ? 32 : 16;  // k per MFMA
+  constexpr int KSTEP = A8 ? (MF == 16 ? 128 : 64) : (MF == 16 ? 32 : 16);  // k per MFMA
   constexpr int KS = BK / KSTEP;             // MFMA k-steps per stage
   constexpr int NACC = MF == 16 ? 4 : 16;
+  constexpr int RD = A8 ? 2 : 1;             // 16-byte LDS reads per fragment
   typedef typename std::conditional<MF == 16, f32x4_t, f32x16_t>::type acc_t;
+  typedef typename std::conditional<A8, i32x8_t, bf16x8_t>::type frag_t;
   // Large wave tiles keep their accumulators in AGPRs (MFMAs issued as
   // inline asm with AGPR operands), leaving the VGPRs to the fragments.
   constexpr bool AGPR_ACC = MF == 32 && !BFP8 && FM * FN * NACC > 128;
+  static_assert(KS >= 1 && BK % KSTEP == 0, "whole MFMA k-steps per stage");
+  static_assert(RD * (FM + FN) < 16, "lgkmcnt range");
   static_assert(MF == 16 || MF == 32, "MFMA shape");
   static_assert(BM * CA % NT == 0 && BN * CB % NT == 0, "tile loads must divide evenly");
   static_assert(FM >= 1 && FN >= 1 && WTM % MF == 0 && WTN % MF == 0, "wave tile");
@@ -294,7 +313,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     // so chunks of rows past the group's count are dropped by the buffer
     // range check: no memory access, zeros in LDS, and those rows are never
     // stored.  Every access stays inside the operands by construction.
-    const i32x4_t rsrc_a = make_rsrc((const char*)a.A + row0 * a.lda * 2, (uint32_t)((int64_t)rows * a.lda * 2));
+    const i32x4_t rsrc_a = make_rsrc((const char*)a.A + row0 * a.lda * ASZ, (uint32_t)((int64_t)rows * a.lda * ASZ));
     const i32x4_t rsrc_b = make_rsrc((const char*)a.B + (int64_t)g * a.b_gstride * BSZ + (int64_t)n0 * a.ldb * BSZ,
                                      (uint32_t)((int64_t)BN * a.ldb * BSZ));
     uint32_t a_off[A_LOADS], b_off[B_LOADS];
@@ -302,7 +321,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     for (int i = 0; i < A_LOADS; ++i) {
       const int q = i * NT + tid;
       const int r = q / CA, s = q % CA;
-      a_off[i] = (uint32_t)(r * a.lda * 2 + (s ^ swz<CA>(r)) * 16);
+      a_off[i] = (uint32_t)(r * a.lda * ASZ + (s ^ swz<CA>(r)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
@@ -315,7 +334,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
       char* sa = smem + slot * STAGE_BYTES;
       char* sb = sa + A_BYTES;
       if (l < A_LOADS)
-        buffer_load_lds_16(rsrc_a, sa + (l * NT + wave * 64) * 16, a_off[l], (uint32_t)((kt0 + kt) * BK * 2));
+        buffer_load_lds_16(rsrc_a, sa + (l * NT + wave * 64) * 16, a_off[l], (uint32_t)((kt0 + kt) * BK * ASZ));
       else
         buffer_load_lds_16(rsrc_b, sb + ((l - A_LOADS) * NT + wave * 64) * 16, b_off[l - A_LOADS],
                            (uint32_t)((kt0 + kt) * BK * BSZ));
@@ -341,41 +360,52 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     // pair, the same conflict-free pattern as the bf16 reads; the activation
     // fragments use the same k assignment (k-step 2u: chunk 2 KC u + 2 h,
     // k-step 2u+1: the next chunk).
-    constexpr int KC = KSTEP / 8;  // 16-byte bf16 chunks per k-step
-    static_assert(!BFP8 || KS % 2 == 0, "fp8 weights pair the k-steps of a stage");
+    //
+    // e4m3 activations (A8): a k-step is KSTEP bytes of a row, KC 16-byte
+    // chunks; the lane of k half / quarter h = lk holds chunks 2h and 2h+1
+    // of the k-step, for both operands.
+    constexpr int KC = A8 ? KSTEP / 16 : KSTEP / 8;  // 16-byte chunks per k-step
+    static_assert(!PAIR || KS % 2 == 0, "fp8 weights pair the k-steps of a stage");
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     uint32_t a_rd[FM], b_rd[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WTM + i * MF + lr;
-      const int c0 = BFP8 ? 2 * lk : lk;
+      const int c0 = (BFP8 || A8) ? 2 * lk : lk;
       a_rd[i] = lds0 + (uint32_t)(r * CA * 16 + ((c0 ^ swz<CA>(r)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int r = wn * WTN + j * MF + lr;
-      b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CB * 16 + ((lk ^ swz<CB>(r)) << 4));
+      const int c0 = A8 ? 2 * lk : lk;
+      b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CB * 16 + ((c0 ^ swz<CB>(r)) << 4));
     }
     // chunk-index XOR of k-step ks (A) and of the k-step pair u (fp8 B)
     auto a_kx = [](int ks) -> uint32_t {
-      return (uint32_t)((BFP8 ? (2 * KC * (ks >> 1) + (ks & 1)) : (KC * ks)) << 4);
+      return (uint32_t)((PAIR ? (2 * KC * (ks >> 1) + (ks & 1)) : (KC * ks)) << 4);
     };
-    auto read_a = [&](int slot, int ks, bf16x8_t (&af)[FM]) {
-      const uint32_t so = (uint32_t)(slot * STAGE_BYTES);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint32_t addr = (a_rd[i] ^ a_kx(ks)) + so;
-        asm volatile("ds_read_b128 %0, %1" : "=v"(af[i]) : "v"(addr));
+    // one fragment: a 16-byte read, or (A8) the two chunks 2h, 2h+1
+    auto read_frag = [](uint32_t addr, frag_t& f) {
+      if constexpr (A8) {
+        i32x4_t lo, hi;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(lo) : "v"(addr));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(hi) : "v"(addr ^ 16u));
+        f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        asm volatile("ds_read_b128 %0, %1" : "=v"(f) : "v"(addr));
       }
     };
-    // bf16: the fragments of k-step q; fp8: the codes of k-step pair q
-    auto read_b = [&](int slot, int q, bf16x8_t (&bfr)[FN]) {
+    auto read_a = [&](int slot, int ks, frag_t (&af)[FM]) {
       const uint32_t so = (uint32_t)(slot * STAGE_BYTES);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint32_t addr = (b_rd[j] ^ (uint32_t)((KC * q) << 4)) + so;
-        asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[j]) : "v"(addr));
-      }
+      for (int i = 0; i < FM; ++i) read_frag((a_rd[i] ^ a_kx(ks)) + so, af[i]);
+    };
+    // bf16 / A8: the fragments of k-step q; fp8 weights with bf16
+    // activations: the codes of k-step pair q
+    auto read_b = [&](int slot, int q, frag_t (&bfr)[FN]) {
+      const uint32_t so = (uint32_t)(slot * STAGE_BYTES);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) read_frag((b_rd[j] ^ (uint32_t)((KC * q) << 4)) + so, bfr[j]);
     };
 
     acc_t acc[FM][FN];
@@ -393,15 +423,28 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // MFMAs of one k-step; for fp8 weights `hi` selects the half of the
-    // pair's codes that belongs to this k-step
-    // MFMAs of one k-step; for fp8 weights `hi` selects the half of the
-    // pair's codes that belongs to this k-step
-    auto mma_sub = [&](const bf16x8_t (&af)[FM], const bf16x8_t (&braw)[FN], bool hi) {
+    // MFMAs of one k-step; for fp8 weights with bf16 activations `hi`
+    // selects the half of the pair's codes that belongs to this k-step
+    auto mma_sub = [&](const frag_t (&af)[FM], const frag_t (&braw)[FN], bool hi) {
+      if constexpr (A8) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          if (wm * WTM + i * MF >= rows) continue;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            if constexpr (MF == 16)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(braw[j], af[i], acc[i][j], 0, 0, 0, 127,
+                                                                           0, 127);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(braw[j], af[i], acc[i][j], 0, 0, 0, 127,
+                                                                          0, 127);
+          }
+        }
+      } else {
       bf16x8_t bfr[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        if constexpr (BFP8) {
+        if constexpr (PAIR) {
           const uint4 q4 = __builtin_bit_cast(uint4, braw[j]);
           const uint32_t w0 = hi ? q4.z : q4.x, w1 = hi ? q4.w : q4.y;
           const bf16x2_t p0 = fp8x2_to_bf16x2<false>(w0), p1 = fp8x2_to_bf16x2<true>(w0);
@@ -426,6 +469,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
         }
       }
+      }
     };
 
     // Pipeline over k-steps (KS per stage) with two fragment buffers: the
@@ -445,7 +489,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     // A fragments alternate per k-step; B fragments per k-step (bf16) or per
     // k-step pair (fp8).  Buffer parities of a stage's k-step 0 come in as
     // compile-time tags (stages are unrolled by two).
-    bf16x8_t fa[2][FM], fb[2][FN];
+    frag_t fa[2][FM], fb[2][FN];
     read_a(0, 0, fa[0]);
     read_b(0, 0, fb[0]);
 
@@ -456,15 +500,15 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int acur = (pa + ks) & 1, anxt = (pa + ks + 1) & 1;
-        const int bcur = BFP8 ? ((pb + (ks >> 1)) & 1) : ((pb + ks) & 1);
-        const int bnxt = BFP8 ? ((pb + ((ks + 1) >> 1)) & 1) : ((pb + ks + 1) & 1);
+        const int bcur = PAIR ? ((pb + (ks >> 1)) & 1) : ((pb + ks) & 1);
+        const int bnxt = PAIR ? ((pb + ((ks + 1) >> 1)) & 1) : ((pb + ks + 1) & 1);
         // does the next k-step start a new B fragment set?
-        const bool nb = BFP8 ? ((ks + 1) % 2 == 0) : true;
+        const bool nb = PAIR ? ((ks + 1) % 2 == 0) : true;
         if (ks + 1 < KS) {
           read_a(slot, ks + 1, fa[anxt]);
-          if (nb) read_b(slot, BFP8 ? (ks + 1) / 2 : ks + 1, fb[bnxt]);
-          if (nb) wait_lgkmcnt<FM + FN>();  // k-step ks has landed; the next may be in flight
-          else wait_lgkmcnt<FM>();
+          if (nb) read_b(slot, PAIR ? (ks + 1) / 2 : ks + 1, fb[bnxt]);
+          if (nb) wait_lgkmcnt<RD * (FM + FN)>();  // k-step ks has landed; the next may be in flight
+          else wait_lgkmcnt<RD * FM>();
         } else if (more) {
           if (kt + STAGES - 1 < KT) wait_vmcnt<(STAGES - 2) * LOADS>();
           else wait_vmcnt<0>();
@@ -472,18 +516,18 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
           if (kt + STAGES < KT) issue(kt + STAGES, slot);
           read_a((kt + 1) % STAGES, 0, fa[anxt]);
           read_b((kt + 1) % STAGES, 0, fb[bnxt]);
-          wait_lgkmcnt<FM + FN>();
+          wait_lgkmcnt<RD * (FM + FN)>();
         } else {
           wait_lgkmcnt<0>();
         }
         __builtin_amdgcn_sched_barrier(0);
-        mma_sub(fa[acur], fb[bcur], BFP8 && (ks & 1));
+        mma_sub(fa[acur], fb[bcur], PAIR && (ks & 1));
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     using P0 = std::integral_constant<int, 0>;
     using PA1 = std::integral_constant<int, (KS & 1)>;
-    using PB1 = std::integral_constant<int, BFP8 ? ((KS / 2) & 1) : (KS & 1)>;
+    using PB1 = std::integral_constant<int, PAIR ? ((KS / 2) & 1) : (KS & 1)>;
     for (int kt = 0; kt < KT; kt += 2) {
       stage(kt, P0{}, P0{});
       if (kt + 1 < KT) stage(kt + 1, PA1{}, PB1{});
@@ -512,7 +556,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
           }
       return;
     }
-    gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
+    gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC, false, A8>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
   };
 
   // whole tiles of the full rounds, then (with a split) this workgroup's
@@ -539,7 +583,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
 // split tile in slice order and runs the epilogue.  Same launch shape as the
 // GEMM (it recomputes the same tail plan); workgroups without a tail tile
 // return at once.
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF, bool A8 = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_fixup_kernel(const GemmArgs a) {
   constexpr int NT = 64 * WM * WN;
@@ -601,7 +645,7 @@ grouped_gemm_fixup_kernel(const GemmArgs a) {
         const float4 u = sum[(i * FN + j) * (NACC / 4) + v];
         acc[i][j][4 * v] = u.x; acc[i][j][4 * v + 1] = u.y; acc[i][j][4 * v + 2] = u.z; acc[i][j][4 * v + 3] = u.w;
       }
-  gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
+  gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC, false, A8>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
 }
 
 // Epilogue of the four-wave kernel, through LDS: bias (+ GeLU) and bf16
@@ -1004,9 +1048,9 @@ constexpr int kSplitGrid = 512;
 // multiple of 8, at least 8), never more than there are tiles.  With a
 // split-K workspace (a.partial) the tail tiles are split and a second
 // kernel reduces them.
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF = 16>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF = 16, bool A8 = false>
 hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial_bytes = 0) {
-  auto kern = grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF>;
+  auto kern = grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF, A8>;
   constexpr int NT = 64 * WM * WN;
   a.m_tiles = (int)ceil_div(rows_cap, BM);
   a.n_tiles = a.N / BN;
@@ -1026,8 +1070,8 @@ hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partial == nullptr) return e;
-  hipLaunchKernelGGL((grouped_gemm_fixup_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF>), dim3((unsigned)grid),
-                     dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((grouped_gemm_fixup_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF, A8>),
+                     dim3((unsigned)grid), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1084,6 +1128,20 @@ static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hi
   }
 }
 
+// e4m3 activations and weights (W8A8); K % 128 == 0.  Row tiles of 128 for
+// every regime with 64+ rows per expert, 16-row tiles for decode.
+template <int EPI>
+static hipError_t run_regime_a8(int regime, const GemmArgs& a, int64_t rows_cap, hipStream_t st, size_t pb) {
+  const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0, k256 = a.K % 256 == 0;
+  if (regime <= 1) {
+    if (n256) return run_bf16<128, 256, 128, 2, 4, 3, true, EPI, 4, 32, true>(a, rows_cap, st, pb);
+    if (n128) return run_bf16<128, 128, 128, 2, 4, 3, true, EPI, 4, 32, true>(a, rows_cap, st, pb);
+    return run_bf16<128, 64, 128, 2, 2, 3, true, EPI, 4, 32, true>(a, rows_cap, st, pb);
+  }
+  if (k256) return run_bf16<16, 64, 256, 1, 4, 5, true, EPI, 1, 16, true>(a, rows_cap, st, pb);
+  return run_bf16<16, 64, 128, 1, 2, 8, true, EPI, 1, 16, true>(a, rows_cap, st, pb);
+}
+
 // Bytes of split-K workspace the expert GEMMs of problem p can use (one
 // float32 tile per workgroup of a persistent launch of up to kSplitGrid).
 // The decode regime (a few rows per expert) streams weights with small
@@ -1107,16 +1165,19 @@ template <int EPI>
 static hipError_t run_expert_gemm(const Problem& p, const GemmArgs& g, int64_t rows_cap, hipStream_t st,
                                   size_t partial_bytes) {
   if (p.act == DT_F32) return run_f32<EPI>(g, rows_cap, st);
+  if (g.a_scale != nullptr) return run_regime_a8<EPI>(gemm_regime(p), g, rows_cap, st, partial_bytes);
   if (p.w == DT_FP8) return run_regime<true, EPI>(gemm_regime(p), g, rows_cap, st, partial_bytes);
   return run_regime<false, EPI>(gemm_regime(p), g, rows_cap, st, partial_bytes);
 }
 
 // h = GeLU(x_perm W1^T + b1) over the expert groups.
+// a_scale: row scales of e4m3 activations (W8A8), or null for bf16 rows.
 hipError_t launch_expert_up(const Problem& p, int64_t rows_cap, const void* x_perm,
                             const int32_t* counts, const int32_t* offsets, const void* W1,
                             const void* b1, const float* s1, void* h, float* partial,
-                            size_t partial_bytes, hipStream_t st) {
+                            size_t partial_bytes, hipStream_t st, const float* a_scale) {
   GemmArgs g = expert_args(p, counts, offsets);
+  g.a_scale = a_scale;
   g.partial = partial;
   g.A = x_perm; g.lda = p.d;
   g.B = W1; g.ldb = p.d; g.b_gstride = (int64_t)p.d_ff * p.d;
@@ -1130,8 +1191,9 @@ hipError_t launch_expert_up(const Problem& p, int64_t rows_cap, const void* x_pe
 hipError_t launch_expert_down(const Problem& p, int64_t rows_cap, const void* h,
                               const int32_t* counts, const int32_t* offsets, const void* W2,
                               const void* b2, const float* s2, void* y_perm, float* partial,
-                              size_t partial_bytes, hipStream_t st) {
+                              size_t partial_bytes, hipStream_t st, const float* a_scale) {
   GemmArgs g = expert_args(p, counts, offsets);
+  g.a_scale = a_scale;
   g.partial = partial;
   g.A = h; g.lda = p.d_ff;
   g.B = W2; g.ldb = p.d_ff; g.b_gstride = (int64_t)p.d * p.d_ff;

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -40,12 +40,12 @@ def test_struct_layout_matches_header():
 #include <stdio.h>
 #include "moe.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_problem),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_problem),
     offsetof(moe_problem, S), offsetof(moe_problem, d), offsetof(moe_problem, d_ff),
     offsetof(moe_problem, E), offsetof(moe_problem, K), offsetof(moe_problem, n_groups),
     offsetof(moe_problem, topk_groups), offsetof(moe_problem, renormalize),
     offsetof(moe_problem, act_dtype), offsetof(moe_problem, w_dtype), offsetof(moe_problem, gate_temperature),
-    offsetof(moe_problem, capacity));
+    offsetof(moe_problem, capacity), offsetof(moe_problem, act_quant));
   return 0;
 }'''
     with tempfile.TemporaryDirectory() as d:
@@ -71,6 +71,10 @@ def prob(**kw):
     (dict(S=-1), M.MOE_ERR_INVALID_ARG),
     (dict(renormalize=2), M.MOE_ERR_INVALID_ARG),
     (dict(capacity=-1), M.MOE_ERR_INVALID_ARG),
+    (dict(act_quant=2), M.MOE_ERR_INVALID_ARG),
+    (dict(act_quant=1), M.MOE_ERR_UNSUPPORTED),                       # bf16 weights
+    (dict(act_quant=1, w="fp8", d=192), M.MOE_ERR_UNSUPPORTED),       # d not a multiple of 128
+    (dict(act_quant=1, act="f32", w="f32"), M.MOE_ERR_UNSUPPORTED),
     (dict(E=12, n_groups=4, topk_groups=2), M.MOE_ERR_INVALID_ARG),   # group of 3: not a power of 2
     (dict(E=16, n_groups=3, topk_groups=1), M.MOE_ERR_INVALID_ARG),   # 16 % 3
     (dict(E=16, n_groups=4, topk_groups=0), M.MOE_ERR_INVALID_ARG),
@@ -205,3 +209,28 @@ def test_apply_capacity_argument_checks():
     # a layer with a capacity needs room for the pair list on top
     assert M.moe_workspace_bytes(p, M.STAGE_LAYER) == M.moe_workspace_bytes(prob(), M.STAGE_LAYER) + need
     assert lib.moe_apply_capacity(ctypes.byref(prob(S=0)), *([None] * 5), None, 0, None) == M.MOE_OK
+
+
+def test_fp8_activation_checks():
+    lib = M.lib()
+    a = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    p = prob(w="fp8", act_quant=1)
+    assert lib.moe_tile_m(ctypes.byref(p)) > 0
+    # the layer needs room for the h codes and the row scales on top
+    plain = M.moe_workspace_bytes(prob(w="fp8"), M.STAGE_LAYER)
+    assert M.moe_workspace_bytes(p, M.STAGE_LAYER) > plain
+    # the stage entry points take bf16 activations only
+    assert lib.moe_permute(ctypes.byref(p), *([a] * 7), a, 1 << 30, None) == M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn(ctypes.byref(p), *([a] * 11), a, 1 << 30, None) == M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_up(ctypes.byref(p), *([a] * 7), None, 0, None) == M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_down(ctypes.byref(p), *([a] * 7), None, 0, None) == M.MOE_ERR_UNSUPPORTED
+    # the row quantiser
+    q = lib.moe_quantize_rows
+    assert q(a, -1, 64, a, a, None) == M.MOE_ERR_INVALID_ARG
+    assert q(a, 4, 60, a, a, None) == M.MOE_ERR_INVALID_ARG
+    assert q(a, 4, 0, a, a, None) == M.MOE_ERR_INVALID_ARG
+    assert q(None, 4, 64, a, a, None) == M.MOE_ERR_INVALID_ARG
+    assert q(a, 4, 64, odd, a, None) == M.MOE_ERR_INVALID_ARG
+    assert q(a, 4, 64, a, None, None) == M.MOE_ERR_INVALID_ARG
+    assert q(None, 0, 64, None, None, None) == M.MOE_OK

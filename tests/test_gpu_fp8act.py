@@ -1,0 +1,136 @@
+"""GPU parity of the fp8-activation (W8A8) path through the C ABI: the row
+quantiser bit-exact against the oracle's, and the whole layer with e4m3
+activations against the oracle's W8A8 layer on the GPU's own scores."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import datagen as D
+import oracle as O
+import sparse_ffn_layer_amd as M
+from tests._util import raw
+from tests.gpu_common import DEV, TOL, gpu_inputs, oracle_view, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def _bf16(a):
+    """float32 numpy -> (bf16 device tensor, the bf16 values as float32)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.to(DEV), t.float().numpy()
+
+
+@pytest.mark.parametrize("rows,n,seed", [(1, 8, 0), (37, 64, 1), (300, 2048, 2), (64, 7168, 3), (16, 14336, 4),
+                                         (1000, 136, 5)])
+def test_quantize_rows_bit_exact(rows, n, seed):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((rows, n)) * np.exp(rng.uniform(-20, 20, (rows, 1)))
+    if rows > 3:
+        v[1] = 0.0                          # zero row
+        v[2, :] = -0.0
+        v[3, ::3] = 0.0                     # zeros inside a row
+        v[3, 1::3] *= -1
+    src, vals = _bf16(v)
+    print(f"quantize rows={rows} n={n}", flush=True)
+    codes, scales = M.moe_quantize_rows(src)
+    sync()
+    o_codes, o_scales = O.quantize_rows_e4m3(vals)
+    np.testing.assert_array_equal(scales.cpu().numpy(), o_scales)
+    np.testing.assert_array_equal(codes.cpu().numpy(), o_codes)
+
+
+def test_quantize_rows_ties_and_subnormals():
+    """Rows whose products v * (448 / amax) land exactly on e4m3 midpoints
+    and in the subnormal range: amax = 448 makes the factor 1."""
+    mags = np.sort(O.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8)))
+    mids = (mags[1:] + mags[:-1]) / 2
+    vals = np.concatenate([mids, -mids, mags, -mags])
+    vals = vals[np.abs(vals.astype(np.float32).astype(np.float64) - vals) == 0]   # exact in bf16 below
+    n = 256
+    rows = []
+    for i in range(0, len(vals), n - 1):
+        chunk = vals[i:i + n - 1]
+        row = np.zeros(n)
+        row[0] = 448.0
+        row[1:1 + len(chunk)] = chunk
+        rows.append(row)
+    v = np.array(rows)
+    src, bv = _bf16(v)
+    keep = np.all(bv.astype(np.float64) == v, axis=1)          # rows that bf16 holds exactly
+    codes, scales = M.moe_quantize_rows(src)
+    sync()
+    o_codes, o_scales = O.quantize_rows_e4m3(bv)
+    assert keep.sum() >= 1
+    np.testing.assert_array_equal(codes.cpu().numpy(), o_codes)
+    np.testing.assert_array_equal(scales.cpu().numpy(), o_scales)
+
+
+def _layer_w8a8(cfg, inp, tokens, cap=0):
+    p = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                       cfg.renormalize, 1.0, cap, 1)
+    logits = torch.empty((cfg.S, cfg.E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((cfg.S, cfg.K), dtype=torch.int32, device=DEV)
+    y = M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                            inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"],
+                            topk_idx_out=idx, logits_out=logits)
+    sync()
+    ov = oracle_view(inp)
+    lg = logits.cpu().numpy()
+    o_idx = O.select_experts(lg, cfg.K, ov["select_bias"], cfg.n_groups, cfg.topk_groups)
+    if not cap:
+        assert np.array_equal(idx.cpu().numpy(), o_idx)
+    ref = O.layer_forward(ov["x"], ov["W_r"], ov["W1"], ov["b1"], ov["W2"], ov["b2"], K=cfg.K, act=cfg.act,
+                          w=cfg.w, select_bias=ov["select_bias"], n_groups=cfg.n_groups,
+                          topk_groups=cfg.topk_groups, renormalize=cfg.renormalize, w1_scale=ov["w1_scale"],
+                          w2_scale=ov["w2_scale"], logits_in=lg, tokens=tokens, capacity=cap, act_quant=True)
+    yg = O.decode(raw(y[torch.from_numpy(np.asarray(tokens)).to(DEV)]), cfg.act)
+    err = np.abs(yg - ref).max() / np.abs(ref).max()
+    print(f"w8a8 {cfg.name} S={cfg.S} rel err {err:.3e}", flush=True)
+    assert err <= TOL["fp8"], err
+    return y
+
+
+@pytest.mark.parametrize("S,E,K,seed", [(2048, 8, 2, 0),    # 512 rows per expert: 128-row tiles
+                                        (640, 16, 2, 1),    # 80 rows per expert
+                                        (24, 8, 2, 2),      # decode: 16-row tiles
+                                        (333, 8, 3, 3)])    # ragged groups
+def test_layer_w8a8_small(S, E, K, seed):
+    base = D.CONFIGS["dsv3_fp8"]
+    cfg = dataclasses.replace(base, name=f"w8a8_{S}_{E}", S=S, d=512, d_ff=768, E=E, K=K, n_groups=1,
+                              topk_groups=1, select_bias_var=0.0, seed=seed)
+    inp = D.make_inputs(cfg, device=DEV)
+    sync()
+    _layer_w8a8(cfg, inp, np.arange(S) if S <= 400 else sample_tokens(S, 96, seed))
+
+
+def test_layer_w8a8_dsv3_full_size():
+    cfg = D.CONFIGS["dsv3_fp8"]
+    inp = gpu_inputs("dsv3_fp8")
+    y8 = _layer_w8a8(cfg, inp, sample_tokens(cfg.S, 8, seed=4))
+    # and it stays close to the bf16-activation layer on the same inputs
+    p = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                       cfg.renormalize)
+    y16 = M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                              inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"])
+    sync()
+    a, b = y8.float(), y16.float()
+    assert float((a - b).abs().max()) <= TOL["fp8"] * float(b.abs().max())
+
+
+def test_layer_w8a8_deterministic():
+    cfg = D.CONFIGS["dsv3_fp8"]
+    inp = gpu_inputs("dsv3_fp8")
+    p = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                       cfg.renormalize, 1.0, 0, 1)
+    args = (p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"], inp["router_bias"],
+            inp["select_bias"], inp["w1_scale"], inp["w2_scale"])
+    y1 = M.moe_layer_forward(*args)
+    y2 = M.moe_layer_forward(*args)
+    sync()
+    assert torch.equal(y1, y2)
