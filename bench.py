@@ -5,11 +5,11 @@ combine) over the workload's S tokens, inputs resident in HBM.  Prints ONE
 JSON line on stdout: MoE-layer tokens/s at the Mixtral-shape prefill workload
 (S=4096, d=4096, d_ff=14336, E=8, K=2, bf16), the roofline of the dominant
 kernel, the decode workload's HBM fraction, the same layer under a
-per-expert capacity, and the CPU oracle's rate on a bounded sample of the
-same workload.
+per-expert capacity, the DeepSeek-shape fp8 layer with fp8 activations, and
+the CPU oracle's rate on a bounded sample of the same workload.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--no-decode] [--no-capacity]
+                       [--no-cpu-baseline] [--no-decode] [--no-capacity] [--no-w8a8]
        python bench.py --pmc-probe [--workload NAME]     (under rocprofv3 --pmc)
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
 """
@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-capacity", action="store_true")
+    ap.add_argument("--no-w8a8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only launch a 1 GiB copy and the expert GEMMs (for rocprofv3 --pmc passes)")
@@ -325,6 +326,41 @@ def capacity_leg(w, M, torch, factor, steps):
             "rerouted_pairs": moved, "dropped_pairs": nd, "drop_rate": round(nd / (c.S * c.K), 5)}
 
 
+def w8a8_leg(D, M, torch, steps, warmup):
+    """The DeepSeek-shape fp8-weight layer with e4m3 activations (W8A8)
+    against the same layer with bf16 activations (W8A16), same inputs.  The
+    expert products stream every touched expert's fp8 weights once, so the
+    weight bytes over the step time are reported next to the HBM peak."""
+    cfg = D.CONFIGS["dsv3_fp8"]
+    inp = D.make_inputs(cfg, "cuda")
+    torch.cuda.synchronize()
+    y = torch.empty((cfg.S, cfg.d), dtype=torch.bfloat16, device="cuda")
+    counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    out = {"workload": cfg.name}
+    for aq in (0, 1):
+        p = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                           cfg.renormalize, 1.0, 0, aq)
+        ws = M.workspace(p, M.STAGE_LAYER, "cuda")
+
+        def step():
+            M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                                inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"], y=y,
+                                expert_counts_out=counts, ws=ws)
+
+        ms = time_calls(torch, step, steps, warmup)
+        out["ms_per_step_w8a8" if aq else "ms_per_step_w8a16"] = round(ms, 4)
+        del ws
+    touched = int((counts > 0).sum().cpu())
+    wbytes = touched * 2 * cfg.d * cfg.d_ff + touched * 4 * (cfg.d + cfg.d_ff)
+    ms = out["ms_per_step_w8a8"]
+    out.update({"tokens_per_s": round(cfg.S / (ms / 1e3), 1), "experts_touched": touched,
+                "expert_weight_bytes": wbytes,
+                "weight_stream_GBps": round(wbytes / (ms / 1e3) / 1e9, 1), "hbm_peak_GBps": PEAK_GBS})
+    del inp
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, w, target_s, torch):
     """The oracle, as it is, on the first n tokens of the same workload."""
     import numpy as np
@@ -410,6 +446,9 @@ def main():
     if not a.no_capacity:
         out["capacity"] = capacity_leg(w, M, torch, 1.25, a.steps)
         log(f"[bench] capacity: {out['capacity']}")
+    if not a.no_w8a8:
+        out["w8a8"] = w8a8_leg(D, M, torch, max(5, a.steps // 2), 3)
+        log(f"[bench] w8a8: {out['w8a8']}")
     if not a.no_decode and cfg.name != "decode":
         dcfg, dw, dms, dstage, dtouched, _ = run_workload("decode", max(a.steps, 100), a.warmup, D, M, torch)
         out["decode"] = {"workload": "decode", "tokens_per_s": round(dcfg.S / (dms / 1e3), 1),
