@@ -133,8 +133,11 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t num_reco
 // address is base + voffset + soffset.
 __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4_t rsrc, lds_void_t* lds, int size, int voffset, int soffset,
                                                 int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// AUX = cache policy bits; 2 marks the load non-temporal ("nt": data read
+// once, streamed past the caches' normal retention).
+template <int AUX = 0>
 __device__ __forceinline__ void buffer_load_lds_16(i32x4_t rsrc, void* lds_base, uint32_t voffset, uint32_t soffset) {
-  llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_void_t*)lds_base, 16, (int)voffset, (int)soffset, 0, 0);
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_void_t*)lds_base, 16, (int)voffset, (int)soffset, 0, AUX);
 }
 
 // 16-byte global -> VGPR load through a buffer resource (range-checked:

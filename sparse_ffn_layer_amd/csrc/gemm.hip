@@ -272,6 +272,9 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   // inline asm with AGPR operands), leaving the VGPRs to the fragments.
   constexpr bool AGPR_ACC = MF == 32 && !BFP8 && FM * FN * NACC > 128;
   static_assert(KS >= 1 && BK % KSTEP == 0, "whole MFMA k-steps per stage");
+  // Decode tiles (a few rows per expert) read every weight exactly once:
+  // those loads are marked non-temporal.
+  constexpr int B_AUX = BM <= 16 ? 2 : 0;
   static_assert(RD * (FM + FN) < 16, "lgkmcnt range");
   static_assert(MF == 16 || MF == 32, "MFMA shape");
   static_assert(BM * CA % NT == 0 && BN * CB % NT == 0, "tile loads must divide evenly");
@@ -336,7 +339,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
       if (l < A_LOADS)
         buffer_load_lds_16(rsrc_a, sa + (l * NT + wave * 64) * 16, a_off[l], (uint32_t)((kt0 + kt) * BK * ASZ));
       else
-        buffer_load_lds_16(rsrc_b, sb + ((l - A_LOADS) * NT + wave * 64) * 16, b_off[l - A_LOADS],
+        buffer_load_lds_16<B_AUX>(rsrc_b, sb + ((l - A_LOADS) * NT + wave * 64) * 16, b_off[l - A_LOADS],
                            (uint32_t)((kt0 + kt) * BK * BSZ));
     };
     auto issue = [&](int kt, int slot) {
@@ -1123,7 +1126,7 @@ static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hi
       if (n128) return run_bf16<128, 128, 64, 2, 4, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
       return run_bf16<128, 64, 64, 2, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
     default:
-      if (k128) return run_bf16<16, 64, 128, 1, 4, 5, BFP8, EPI, 1>(a, rows_cap, st, pb);
+      if (k128) return run_bf16<16, 64, 128, 1, 4, 3, BFP8, EPI, 1>(a, rows_cap, st, pb);
       return run_bf16<16, 64, 64, 1, 2, 8, BFP8, EPI, 1>(a, rows_cap, st, pb);  // 128 threads: A tile is 128 chunks
   }
 }
