@@ -361,6 +361,51 @@ def w8a8_leg(D, M, torch, steps, warmup):
     return out
 
 
+def cpu_loops_baseline(cfg, w, target_s, torch):
+    """The plain C++ loops of oracle/moe_oracle_ref.cpp (OpenMP over tokens,
+    double precision) on the first n tokens of the same workload; the
+    experts' weights are decoded to double before the timed call."""
+    import numpy as np
+
+    from oracle import cref
+    if not os.path.exists(cref.LIB_PATH):
+        return None
+
+    def host(t, dt):
+        t = t.detach().cpu()
+        if t.dtype == torch.bfloat16:
+            return cref.decode(t.view(torch.int16).numpy().view(np.uint16), "bf16")
+        if t.dtype == torch.float8_e4m3fn:
+            return cref.decode(t.view(torch.uint8).numpy(), "fp8")
+        return t.double().numpy()
+
+    inp = w.inp
+    if cfg.w == "fp8":
+        return None     # the loops take the fp8 scales folded in; measured on bf16 workloads only
+    W1, W2 = host(inp["W1"], cfg.w), host(inp["W2"], cfg.w)
+    b1, b2 = host(inp["b1"], cfg.act), host(inp["b2"], cfg.act)
+    wr = host(inp["W_r"], cfg.act)
+    rb = None if inp["router_bias"] is None else inp["router_bias"].cpu().numpy()
+    sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+    xall = host(inp["x"], cfg.act)
+
+    def run(n):
+        t0 = time.perf_counter()
+        cref.layer_forward(xall[:n], wr, W1, b1, W2, b2, K=cfg.K, router_bias=rb, select_bias=sb,
+                           n_groups=cfg.n_groups, topk_groups=cfg.topk_groups, renormalize=cfg.renormalize)
+        return time.perf_counter() - t0
+
+    n = min(cfg.S, 16)
+    t = run(n)
+    while t < 0.5 * target_s and n < cfg.S:
+        n = int(min(cfg.S, n * min(8.0, max(2.0, target_s / max(t, 1e-3)))))
+        t = run(n)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.S} tokens of {cfg.name}: plain C++ loops (double, OpenMP), "
+                      f"weights decoded beforehand; {t:.1f}s", "seconds": round(t, 2)}
+
+
 def cpu_baseline(cfg, w, target_s, torch):
     """The oracle, as it is, on the first n tokens of the same workload."""
     import numpy as np
@@ -457,6 +502,9 @@ def main():
         del dw
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, w, a.cpu_seconds, torch)
+        loops = cpu_loops_baseline(cfg, w, a.cpu_seconds / 2, torch)
+        if loops is not None:
+            out["cpu_baseline"]["cpp_loops"] = loops
     print(json.dumps(out), flush=True)
 
 
