@@ -84,6 +84,20 @@ def test_apply_capacity_matches_oracle(case):
     assert np.array_equal(idx, idx2) and np.array_equal(gate, gate2) and dropped == dropped2
 
 
+@pytest.mark.parametrize("S,E,K,cap", [(16, 16, 1, 1), (19, 16, 1, 1), (96, 64, 2, 2), (300, 128, 4, 3),
+                                        (64, 64, 1, 1)])
+def test_many_rounds(S, E, K, cap):
+    """Every token ranks the experts in the same order, so each round fills
+    only a few experts: 16 to 64 rounds, past the fixed number of rerouting
+    launches, so the single-workgroup finisher runs the rest."""
+    lg = np.tile(-np.arange(E, dtype=np.float32), (S, 1))
+    _, idx, gate, dropped = _run(S, E, K, 1, 1, lg, None, cap, 1, 1.0)
+    o_idx, o_gate, o_drop = O.apply_capacity(lg, O.select_experts(lg, K), cap)
+    assert np.array_equal(idx, o_idx)
+    assert dropped == o_drop
+    np.testing.assert_allclose(gate, o_gate, rtol=0, atol=GATE_TOL)
+
+
 @pytest.mark.parametrize("cap_of", [lambda S, K: 0, lambda S, K: S * K], ids=["zero", "SK"])
 def test_no_limit_keeps_routing_and_gates_bit_for_bit(cap_of):
     S, E, K, G, TG = 700, 64, 6, 8, 3
