@@ -96,13 +96,15 @@ def _layer_w8a8(cfg, inp, tokens, cap=0):
     return y
 
 
-@pytest.mark.parametrize("S,E,K,seed", [(2048, 8, 2, 0),    # 512 rows per expert: 128-row tiles
-                                        (640, 16, 2, 1),    # 80 rows per expert
-                                        (24, 8, 2, 2),      # decode: 16-row tiles
-                                        (333, 8, 3, 3)])    # ragged groups
-def test_layer_w8a8_small(S, E, K, seed):
+@pytest.mark.parametrize("S,E,K,seed,d,d_ff", [(2048, 8, 2, 0, 512, 768),    # 512 rows per expert: 128-row tiles
+                                               (640, 16, 2, 1, 512, 768),    # 80 rows per expert
+                                               (24, 8, 2, 2, 512, 768),      # decode: 16-row tiles, k % 256 == 0
+                                               (333, 8, 3, 3, 512, 768),     # ragged groups
+                                               (400, 8, 2, 4, 640, 384),     # 128-wide channel tiles
+                                               (20, 8, 2, 5, 640, 384)])     # decode with k % 256 != 0
+def test_layer_w8a8_small(S, E, K, seed, d, d_ff):
     base = D.CONFIGS["dsv3_fp8"]
-    cfg = dataclasses.replace(base, name=f"w8a8_{S}_{E}", S=S, d=512, d_ff=768, E=E, K=K, n_groups=1,
+    cfg = dataclasses.replace(base, name=f"w8a8_{S}_{E}", S=S, d=d, d_ff=d_ff, E=E, K=K, n_groups=1,
                               topk_groups=1, select_bias_var=0.0, seed=seed)
     inp = D.make_inputs(cfg, device=DEV)
     sync()
@@ -134,3 +136,14 @@ def test_layer_w8a8_deterministic():
     y2 = M.moe_layer_forward(*args)
     sync()
     assert torch.equal(y1, y2)
+
+
+def test_layer_w8a8_with_capacity():
+    """fp8 activations and a per-expert capacity together: the capacity
+    decides the routing, the W8A8 products run on the kept pairs."""
+    base = D.CONFIGS["dsv3_fp8"]
+    cfg = dataclasses.replace(base, name="w8a8_cap", S=640, d=512, d_ff=768, E=16, K=2, n_groups=1, topk_groups=1,
+                              select_bias_var=0.0, router_offset="normal", offset_beta=1.0, seed=7)
+    inp = D.make_inputs(cfg, device=DEV)
+    sync()
+    _layer_w8a8(cfg, inp, np.arange(0, cfg.S, 3), cap=60)
