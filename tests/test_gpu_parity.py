@@ -306,6 +306,8 @@ def test_layer_forward(name):
     dict(S=1500, d=256, d_ff=384, E=8, K=2),                       # prefill regime, ragged tiles
     dict(S=333, d=128, d_ff=256, E=32, K=3, act="f32", w="f32"),   # fp32 path
     dict(S=64, d=512, d_ff=256, E=128, K=4, w="fp8"),              # mid regime fp8
+    dict(S=200, d=128, d_ff=128, E=512, K=8, n_groups=16, topk_groups=4),  # largest E, 16 groups
+    dict(S=24, d=128, d_ff=128, E=128, K=64),                      # largest K
 ])
 def test_layer_edge_cases(kw):
     cfg = D.MoEConfig("edge", **kw)
