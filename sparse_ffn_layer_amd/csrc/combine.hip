@@ -7,9 +7,10 @@
 // "MoE 混合专家推理" (plumephp.com), one MoE forward: the chosen experts'
 // results are weighted by their scores and added.
 //
-// One wavefront per token reads its K rows of y_perm (through inv_perm) in
-// slot order and accumulates in float32 with no atomics, so the result does
-// not depend on scheduling.
+// One block per token: each lane owns 16-byte column chunks of the token's
+// row, reads its K rows of y_perm (through inv_perm) in slot order and
+// accumulates in float32 with no atomics, so the result does not depend on
+// scheduling or on how the row is split over lanes.
 #include "common.h"
 
 namespace sfl {
@@ -21,10 +22,10 @@ __global__ void __launch_bounds__(64 * COMBINE_WAVES)
 combine_kernel(int64_t S, int K, int row_vecs, const uint4* __restrict__ y_perm,
                const int32_t* __restrict__ inv_perm, const float* __restrict__ gate,
                uint4* __restrict__ y) {
-  const int64_t t = (int64_t)blockIdx.x * COMBINE_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t t = blockIdx.x;
   if (t >= S) return;
   constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte vector
-  for (int i = lane_id(); i < row_vecs; i += 64) {
+  for (int i = threadIdx.x; i < row_vecs; i += 64 * COMBINE_WAVES) {
     float acc[EPV];
 #pragma unroll
     for (int q = 0; q < EPV; ++q) acc[q] = 0.f;
@@ -63,7 +64,7 @@ hipError_t launch_combine(const Problem& p, const void* y_perm, const int32_t* i
                           const float* gate, void* y, hipStream_t st) {
   const bool bf = p.act == DT_BF16;
   const int row_vecs = p.d * (bf ? 2 : 4) / 16;
-  const unsigned grid = (unsigned)ceil_div(p.S, COMBINE_WAVES);
+  const unsigned grid = (unsigned)p.S;  // one block per token
   if (bf)
     combine_kernel<true><<<grid, 64 * COMBINE_WAVES, 0, st>>>(p.S, p.K, row_vecs, (const uint4*)y_perm,
                                                              inv_perm, gate, (uint4*)y);

@@ -19,6 +19,7 @@
 //               rank among equal experts inside a wave, LDS counters carry
 //               the rank across waves and rounds) and writes perm/inv_perm.
 //   4. gather:  x_perm[inv_perm[p]] = x[p / K], one wave per row.
+// When all pairs fit one block, steps 1-3 run as one single-block kernel.
 #include "common.h"
 
 namespace sfl {
@@ -162,6 +163,90 @@ permute_scatter_kernel(const int32_t* __restrict__ idx, int64_t pairs, int E, in
   }
 }
 
+// All pairs in one block (a small batch): count, scan and scatter in one
+// workgroup -- the steps above without their cross-block parts -- so a
+// decode step pays one launch instead of three.
+__global__ void __launch_bounds__(PERM_THREADS)
+permute_single_kernel(const int32_t* __restrict__ idx, int64_t pairs, int E, int ebits, int tile_m,
+                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                      int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  __shared__ int run[PERM_MAX_E];
+  __shared__ int dns[PERM_MAX_E];
+  __shared__ int ofs[PERM_MAX_E];
+  __shared__ int wc[PERM_THREADS / 64][PERM_MAX_E + 1];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += PERM_THREADS) {
+    run[e] = 0;
+#pragma unroll
+    for (int w = 0; w < PERM_THREADS / 64; ++w) wc[w][e] = 0;
+  }
+  __syncthreads();
+  // 1. histogram (ids outside [0, E) are ignored)
+  for (int64_t p = threadIdx.x; p < pairs; p += PERM_THREADS) {
+    const unsigned e = (unsigned)idx[p];
+    if (e < (unsigned)E) atomicAdd(&run[e], 1);
+  }
+  __syncthreads();
+  // 2. dense and tile-padded exclusive scans over the experts (wave 0)
+  if (wave == 0) {
+    int cd = 0, cp = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < E ? run[e] : 0;
+      const int cpad = (c + tile_m - 1) / tile_m * tile_m;
+      int id = c, ip = cpad;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(id, o, 64), w = __shfl_up(ip, o, 64);
+        if (lane >= o) { id += u; ip += w; }
+      }
+      if (e < E) {
+        counts[e] = c;
+        dns[e] = cd + id - c;
+        ofs[e] = cp + ip - cpad;
+        offsets[e] = cp + ip - cpad;
+      }
+      cd += __shfl(id, 63, 64);
+      cp += __shfl(ip, 63, 64);
+    }
+    if (lane == 0) offsets[E] = cp;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += PERM_THREADS) run[e] = 0;
+  __syncthreads();
+  // 3. stable ranks in pair order (as permute_scatter_kernel with one block)
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t q0 = 0; q0 < pairs; q0 += PERM_THREADS) {
+    const int64_t p = q0 + threadIdx.x;
+    int e = p < pairs ? idx[p] : E;
+    if (e < 0 || e > E) e = E;  // E: sentinel for lanes past the end and bad ids
+    const bool valid = e < E;
+    if (p < pairs && !valid) inv_perm[p] = -1;
+    uint64_t peers = ~0ull;
+    for (int bit = 0; bit < ebits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t bal = __ballot(set);
+      peers &= set ? bal : ~bal;
+    }
+    const int rank_w = __popcll(peers & lt);
+    const bool leader = (peers & lt) == 0;
+    if (valid && leader) wc[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pos = run[e] + rank_w;
+      for (int w = 0; w < wave; ++w) pos += wc[w][e];
+      perm[dns[e] + pos] = (int32_t)p;
+      inv_perm[p] = ofs[e] + pos;
+    }
+    __syncthreads();
+    if (valid && leader) {
+      atomicAdd(&run[e], __popcll(peers));
+      wc[wave][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
 // x_perm[inv_perm[p]] = x[p / K]; one wave per pair, 16-byte copies.
 __global__ void __launch_bounds__(PERM_THREADS)
 gather_rows_kernel(const uint4* __restrict__ x, int64_t pairs, int K, int row_vecs,
@@ -192,15 +277,21 @@ hipError_t launch_permute(const Problem& p, int tile_m, const int32_t* idx, cons
   int ebits = 0;
   while ((1 << ebits) <= p.E) ++ebits;  // enough bits for 0..E (E is the sentinel)
 
-  permute_count_kernel<<<nb, PERM_THREADS, 0, st>>>(idx, pairs, p.E, chunk, hist);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const size_t lds = ((size_t)p.E * nb + 2 * (size_t)p.E) * sizeof(int);
-  permute_scan_kernel<<<1, SCAN_THREADS, lds, st>>>(p.E, nb, tile_m, hist, counts, dense, offsets);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  permute_scatter_kernel<<<nb, PERM_THREADS, 0, st>>>(idx, pairs, p.E, ebits, chunk, hist, dense,
-                                                     offsets, perm, inv_perm);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipError_t err;
+  if (nb == 1) {
+    permute_single_kernel<<<1, PERM_THREADS, 0, st>>>(idx, pairs, p.E, ebits, tile_m, counts, offsets, perm,
+                                                      inv_perm);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  } else {
+    permute_count_kernel<<<nb, PERM_THREADS, 0, st>>>(idx, pairs, p.E, chunk, hist);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const size_t lds = ((size_t)p.E * nb + 2 * (size_t)p.E) * sizeof(int);
+    permute_scan_kernel<<<1, SCAN_THREADS, lds, st>>>(p.E, nb, tile_m, hist, counts, dense, offsets);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    permute_scatter_kernel<<<nb, PERM_THREADS, 0, st>>>(idx, pairs, p.E, ebits, chunk, hist, dense,
+                                                       offsets, perm, inv_perm);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (x_perm != nullptr) {
     const int esz = p.act == DT_F32 ? 4 : 2;
     const int row_vecs = p.d * esz / 16;

@@ -23,7 +23,7 @@
 
 namespace sfl {
 
-constexpr int ROUTER_WAVES = 4;  // tokens per 256-thread block
+constexpr int ROUTER_WAVES = 4;  // waves of a router block
 
 // Select K experts from this token's logits and write indices and gates.
 // lg[r]: unbiased logit of expert r*64 + lane (-inf where that is >= E).
@@ -68,29 +68,40 @@ __device__ __forceinline__ void select_and_gate(const float (&lg)[R], int E, int
   }
 }
 
-// Scores x . W_r (+ router_bias) on the vector ALUs, then selection.  EC
-// experts are accumulated per pass over the token row.
-template <typename T, int EC, int R>
+// Scores x . W_r (+ router_bias) on the vector ALUs, then selection.  WPT
+// waves per token (ROUTER_WAVES / WPT tokens per block): wave w of a token
+// sums the spans w, w + WPT, ... of the row (a span is one 16-byte load per
+// lane) for every expert, EC experts per pass; the partial sums meet in LDS
+// and are added in wave order, so the scores do not depend on scheduling;
+// the token's first wave then selects.  Splitting a row over several waves
+// shortens the chain of dependent loads each wave waits on, which is what a
+// small batch pays for; a large batch has waves enough to hide it (WPT = 1).
+template <typename T, int EC, int R, int WPT>
 __global__ void __launch_bounds__(64 * ROUTER_WAVES)
 router_fused_kernel(int64_t S, int d, int E, int K, const T* __restrict__ x,
                     const T* __restrict__ Wr, const float* __restrict__ rbias,
                     const float* __restrict__ sbias, int n_groups, int topk_groups, int renorm,
                     float inv_tau, float* __restrict__ logits_out, int32_t* __restrict__ idx,
                     float* __restrict__ gate) {
+  static_assert(ROUTER_WAVES % WPT == 0, "whole tokens per block");
+  __shared__ float part[ROUTER_WAVES][64 * R];
   const int lane = lane_id();
-  const int64_t t = (int64_t)blockIdx.x * ROUTER_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (t >= S) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = wave % WPT;  // this wave's share of the token's row
+  const int64_t t = (int64_t)blockIdx.x * (ROUTER_WAVES / WPT) + wave / WPT;
+  const bool live = t < S;     // every wave still reaches the barrier
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
-  const T* xr = x + t * d;
-  float lg[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) lg[r] = -INFINITY;
+  constexpr int SPAN = 64 * VEC;
+  const T* xr = x + (live ? t : 0) * d;
 
-  for (int e0 = 0; e0 < E; e0 += EC) {
+  for (int e0 = 0; e0 < E && live; e0 += EC) {
     float acc[EC];
 #pragma unroll
     for (int j = 0; j < EC; ++j) acc[j] = 0.f;
-    for (int i0 = lane * VEC; i0 < d; i0 += 64 * VEC) {
+#pragma unroll 2
+    for (int s0 = sub * SPAN; s0 < d; s0 += WPT * SPAN) {
+      const int i0 = s0 + lane * VEC;
+      if (i0 >= d) continue;
       float xv[VEC];
       if constexpr (sizeof(T) == 2) {
         const uint4 raw = *reinterpret_cast<const uint4*>(xr + i0);
@@ -126,13 +137,21 @@ router_fused_kernel(int64_t S, int d, int E, int K, const T* __restrict__ x,
 #pragma unroll
     for (int j = 0; j < EC; ++j) {
       const float tot = wave_sum(acc[j]);
-      const int e = e0 + j;
-      if (e < E) {
-        const float l = rbias != nullptr ? tot + rbias[e] : tot;
+      if (lane == 0 && e0 + j < E) part[wave][e0 + j] = tot;
+    }
+  }
+  __syncthreads();
+  if (sub != 0 || !live) return;
+  float lg[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (r * 64 + lane == e) lg[r] = l;
-      }
+  for (int r = 0; r < R; ++r) {
+    const int e = r * 64 + lane;
+    lg[r] = -INFINITY;
+    if (e < E) {
+      float l = part[wave][e];
+#pragma unroll
+      for (int w = 1; w < WPT; ++w) l += part[wave + w][e];
+      lg[r] = rbias != nullptr ? l + rbias[e] : l;
     }
   }
   if (logits_out != nullptr) {
@@ -289,12 +308,20 @@ static hipError_t launch_fused_T(const Problem& p, const void* x, const void* Wr
                                  const float* sb, float* lo, int32_t* idx, float* gate,
                                  hipStream_t st) {
   const int R = (p.E + 63) / 64;
-  const dim3 grid((unsigned)ceil_div(p.S, ROUTER_WAVES)), block(64 * ROUTER_WAVES);
-#define SFL_FUSED(RR)                                                                           \
-  router_fused_kernel<T, EC, RR><<<grid, block, 0, st>>>(p.S, p.d, p.E, p.K, (const T*)x,      \
-                                                         (const T*)Wr, rb, sb, p.n_groups,      \
-                                                         p.topk_groups, p.renormalize, p.inv_tau, \
-                                                         lo, idx, gate)
+  // a row per wave once the batch alone fills the chip with waves
+  const bool split = p.S < 2048;
+  const dim3 grid((unsigned)(split ? p.S : ceil_div(p.S, ROUTER_WAVES))), block(64 * ROUTER_WAVES);
+#define SFL_FUSED(RR)                                                                              \
+  do {                                                                                             \
+    if (split)                                                                                     \
+      router_fused_kernel<T, EC, RR, ROUTER_WAVES><<<grid, block, 0, st>>>(                        \
+          p.S, p.d, p.E, p.K, (const T*)x, (const T*)Wr, rb, sb, p.n_groups, p.topk_groups,        \
+          p.renormalize, p.inv_tau, lo, idx, gate);                                                \
+    else                                                                                           \
+      router_fused_kernel<T, EC, RR, 1><<<grid, block, 0, st>>>(                                   \
+          p.S, p.d, p.E, p.K, (const T*)x, (const T*)Wr, rb, sb, p.n_groups, p.topk_groups,        \
+          p.renormalize, p.inv_tau, lo, idx, gate);                                                \
+  } while (0)
   switch (R) {
     case 1: SFL_FUSED(1); break;
     case 2: SFL_FUSED(2); break;

@@ -149,6 +149,39 @@ def test_permute_shapes(S, E, K):
     _permute_case(E, K, idx)
 
 
+@pytest.mark.parametrize("S,E,K", [(15, 8, 2), (512, 8, 2), (513, 8, 2), (40, 512, 8)])
+def test_permute_with_dropped_pairs(S, E, K):
+    """Pairs with an index of -1 (dropped by a capacity) or outside [0, E) get
+    no row (inv_perm -1) and do not count.  The expectation is the oracle's
+    permutation with those pairs sent to an extra expert E, which sorts after
+    every real expert and so leaves their counts, offsets and order alone.
+    512 x 2 pairs still fit the single-block dispatch, 513 x 2 do not."""
+    rng = np.random.default_rng(S * 7 + E)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(S)]).astype(np.int32)
+    drop = rng.random(idx.shape) < 0.1
+    idx[drop] = -1
+    idx[0, 0], idx[-1, -1] = E, E + 5  # out of range
+    print(f"permute with dropped pairs S={S} E={E} K={K} dropped={(idx < 0).sum() + 2}", flush=True)
+    cfg = D.MoEConfig("p", S=S, d=64, d_ff=64, E=E, K=K)
+    p = problem(cfg)
+    tm = M.moe_tile_m(p)
+    x = D.tokens(cfg, DEV)
+    counts, offsets, perm, inv, x_perm = M.moe_permute(p, torch.from_numpy(idx).to(DEV), x)
+    sync()
+    bad = (idx < 0) | (idx >= E)
+    ref = O.permute(np.where(bad, E, idx), E + 1, tm)
+    kept = int((~bad).sum())
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"][:E])
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"][:E + 1])
+    assert np.array_equal(perm.cpu().numpy()[:kept], ref["perm"][:kept])
+    inv_ref = np.where(bad.reshape(-1), -1, ref["inv_perm"])
+    assert np.array_equal(inv.cpu().numpy(), inv_ref)
+    good = np.flatnonzero(~bad.reshape(-1))
+    rows = torch.from_numpy(inv_ref[good].astype(np.int64)).to(DEV)
+    tok = torch.from_numpy(good // K).to(DEV)
+    assert torch.equal(x_perm[rows].view(torch.int16), x[tok].view(torch.int16))
+
+
 def test_permute_all_tokens_one_expert_set():
     S, E, K = 4099, 64, 4
     idx = np.tile(np.arange(K, dtype=np.int32)[::-1], (S, 1)).copy()
