@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-capacity", action="store_true")
     ap.add_argument("--no-w8a8", action="store_true")
+    ap.add_argument("--no-skew", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only launch a 1 GiB copy and the expert GEMMs (for rocprofv3 --pmc passes)")
@@ -274,6 +275,23 @@ def roofline(cfg, stage_ms, touched, workload):
             "avg_launch_ms": round(stage_ms[name], 4), "algorithmic_flops": fl, "algorithmic_bytes": by}
 
 
+def layer_fractions(cfg, ms, touched, mfma_dtype):
+    """Layer-level fractions of the two roofs: algorithmic layer flops
+    (4 S K d d_ff + 2 S d E) over the step time against the dense MFMA peak
+    of mfma_dtype, and algorithmic layer bytes (x and y once, W_r, and every
+    touched expert's weights, scales and biases once) against the HBM peak."""
+    a = 2 if cfg.act == "bf16" else 4
+    w = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.w]
+    sc = 4 if cfg.w == "fp8" else 0
+    fl = 4.0 * cfg.S * cfg.K * cfg.d * cfg.d_ff + 2.0 * cfg.S * cfg.d * cfg.E
+    by = (2 * cfg.S * cfg.d * a + cfg.E * cfg.d * a
+          + touched * (2 * cfg.d * cfg.d_ff * w + (cfg.d + cfg.d_ff) * (a + sc)))
+    sec = ms / 1e3
+    return {"algorithmic_flops": fl, "algorithmic_bytes": by,
+            "mfma_frac": round(fl / sec / (PEAK_TFLOPS[mfma_dtype] * 1e12), 4), "mfma_peak_dtype": mfma_dtype,
+            "hbm_frac": round(by / sec / (PEAK_GBS * 1e9), 4)}
+
+
 def run_workload(name, steps, warmup, D, M, torch):
     cfg = D.CONFIGS[name]
     w = Workload(cfg, D, M, torch)
@@ -355,7 +373,9 @@ def w8a8_leg(D, M, torch, steps, warmup):
     ms = out["ms_per_step_w8a8"]
     out.update({"tokens_per_s": round(cfg.S / (ms / 1e3), 1), "experts_touched": touched,
                 "expert_weight_bytes": wbytes,
-                "weight_stream_GBps": round(wbytes / (ms / 1e3) / 1e9, 1), "hbm_peak_GBps": PEAK_GBS})
+                "weight_stream_GBps": round(wbytes / (ms / 1e3) / 1e9, 1), "hbm_peak_GBps": PEAK_GBS,
+                "layer_w8a8": layer_fractions(cfg, ms, touched, "fp8"),
+                "layer_w8a16": layer_fractions(cfg, out["ms_per_step_w8a16"], touched, "bf16")})
     del inp
     torch.cuda.empty_cache()
     return out
@@ -484,6 +504,7 @@ def main():
                    "weights": cfg.w, "max_over_mean_load": round(float(counts.max()) / mean, 3),
                    "experts_touched": touched},
         "roofline": roofline(cfg, stage_ms, touched, cfg.name),
+        "layer": layer_fractions(cfg, ms, touched, "bf16" if cfg.act == "bf16" else "f32"),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "layer_tflops": round(4.0 * cfg.S * cfg.K * cfg.d * cfg.d_ff / (ms / 1e3) / 1e12, 2),
     }
@@ -498,8 +519,24 @@ def main():
         dcfg, dw, dms, dstage, dtouched, _ = run_workload("decode", max(a.steps, 100), a.warmup, D, M, torch)
         out["decode"] = {"workload": "decode", "tokens_per_s": round(dcfg.S / (dms / 1e3), 1),
                          "ms_per_step": round(dms, 4), "roofline": roofline(dcfg, dstage, dtouched, "decode"),
+                         "layer": layer_fractions(dcfg, dms, dtouched, "bf16"),
                          "stage_ms": {k: round(v, 4) for k, v in dstage.items()}}
         del dw
+    if not a.no_skew and cfg.name != "zipf_skew":
+        zcfg, zw, zms, zstage, ztouched, zcounts = run_workload("zipf_skew", a.steps, a.warmup, D, M, torch)
+        gemm_ms = zstage["expert_up"] + zstage["expert_down"]
+        ffn_flops = 4.0 * zcfg.S * zcfg.K * zcfg.d * zcfg.d_ff
+        out["zipf_skew"] = {"workload": "zipf_skew", "tokens_per_s": round(zcfg.S / (zms / 1e3), 1),
+                            "ms_per_step": round(zms, 4),
+                            "max_over_mean_load": round(float(zcounts.max()) / (zcfg.S * zcfg.K / zcfg.E), 3),
+                            "empty_experts": zcfg.E - ztouched,
+                            "roofline": roofline(zcfg, zstage, ztouched, "zipf_skew"),
+                            "gemms_mfma_frac": round(ffn_flops / (gemm_ms / 1e3) / (PEAK_TFLOPS["bf16"] * 1e12), 4),
+                            "layer": layer_fractions(zcfg, zms, ztouched, "bf16"),
+                            "stage_ms": {k: round(v, 4) for k, v in zstage.items()}}
+        log(f"[bench] zipf_skew: {zms:.3f} ms/step, stages {out['zipf_skew']['stage_ms']}")
+        del zw
+        torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, w, a.cpu_seconds, torch)
         loops = cpu_loops_baseline(cfg, w, a.cpu_seconds / 2, torch)
