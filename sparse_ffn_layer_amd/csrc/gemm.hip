@@ -302,50 +302,92 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   const int KT_ALL = a.K / BK;
   const TailPlan tp = tail_plan(T, xcd, nx, a.partial != nullptr && KT_ALL >= 16);
 
-  // one tile: k-tiles [kt0, kt1); part != null: store the raw float32
-  // accumulators there (a split-K slice) instead of running the epilogue
-  auto run_tile = [&](int64_t L, int kt0, int kt1, float* part) {
+  // Work items: whole tiles of the full rounds, then (with a split) this
+  // workgroup's k-slice of a tail tile.  Global -> LDS copies are buffer
+  // loads with a scalar resource per tile (its base is the tile's first row
+  // / channel) and one 32-bit offset per copied chunk; the k position goes
+  // into the scalar offset.  The resources cover exactly the tile's valid
+  // rows (num_records in bytes), so chunks of rows past the group's count
+  // are dropped by the buffer range check: no memory access, zeros in LDS,
+  // and those rows are never stored.  Every access stays inside the
+  // operands by construction.
+  struct Item {
     int64_t row0;
-    int n0, g, rows;
-    if (!tile_coords<BM, BN, GM>(a, m_used, L, row0, n0, g, rows)) return;
+    int n0, g, rows, kt0, kt1;
+    float* part;     // split-K slice: raw float32 accumulators go here
+    i32x4_t ra, rb;  // buffer resources of the tile's A rows and B rows
+  };
+  const int64_t loop_end = tp.split ? tp.full_end : tp.t_hi;
+  const bool has_slice = tp.split && xj < tp.tail * tp.split;
+  // the first valid item at tile index >= L (L is advanced past it)
+  auto next_item = [&](int64_t& L, Item& it) -> bool {
+    for (;; L += nx) {
+      int64_t Lt = L;
+      it.kt0 = 0;
+      it.kt1 = KT_ALL;
+      it.part = nullptr;
+      if (L >= loop_end) {
+        if (!has_slice || L - nx >= loop_end) return false;  // the slice comes once, after the whole tiles
+        const int tau = xj / tp.split, sig = xj % tp.split;
+        Lt = tp.full_end + tau;
+        it.kt0 = KT_ALL * sig / tp.split;
+        it.kt1 = KT_ALL * (sig + 1) / tp.split;
+        it.part = a.partial + (size_t)blockIdx.x * (BM * BN);
+      }
+      if (!tile_coords<BM, BN, GM>(a, m_used, Lt, it.row0, it.n0, it.g, it.rows)) continue;
+      auto uni = [](i32x4_t v) {
+        return i32x4_t{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                       __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w)};
+      };
+      it.ra = uni(make_rsrc((const char*)a.A + it.row0 * a.lda * ASZ, (uint32_t)((int64_t)it.rows * a.lda * ASZ)));
+      it.rb = uni(make_rsrc((const char*)a.B + (int64_t)it.g * a.b_gstride * BSZ + (int64_t)it.n0 * a.ldb * BSZ,
+                            (uint32_t)((int64_t)BN * a.ldb * BSZ)));
+      L += nx;
+      return true;
+    }
+  };
+  // per-thread chunk offsets (the same for every tile)
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int q = i * NT + tid;
+    const int r = q / CA, s = q % CA;
+    a_off[i] = (uint32_t)(r * a.lda * ASZ + (s ^ swz<CA>(r)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int q = i * NT + tid;
+    const int r = q / CB, s = q % CB;
+    b_off[i] = (uint32_t)(r * a.ldb * BSZ + (s ^ swz<CB>(r)) * 16);
+  }
+  // copy l of stage kt of item t into LDS slot `slot`: the A chunks first,
+  // then the B chunks
+  auto issue_one = [&](const Item& t, int kt, int slot, int l) {
+    char* sa = smem + slot * STAGE_BYTES;
+    char* sb = sa + A_BYTES;
+    if (l < A_LOADS)
+      buffer_load_lds_16(t.ra, sa + (l * NT + wave * 64) * 16, a_off[l], (uint32_t)((t.kt0 + kt) * BK * ASZ));
+    else
+      buffer_load_lds_16<B_AUX>(t.rb, sb + ((l - A_LOADS) * NT + wave * 64) * 16, b_off[l - A_LOADS],
+                                (uint32_t)((t.kt0 + kt) * BK * BSZ));
+  };
+  auto issue = [&](const Item& t, int kt, int slot) {
+#pragma unroll
+    for (int l = 0; l < LOADS; ++l) issue_one(t, kt, slot, l);
+  };
 
-    // Global -> LDS copies: buffer loads with a scalar resource per tile
-    // (its base is the tile's first row / channel) and one 32-bit offset
-    // per copied chunk; the k position goes into the scalar offset.  The
-    // resources cover exactly the tile's valid rows (num_records in bytes),
-    // so chunks of rows past the group's count are dropped by the buffer
-    // range check: no memory access, zeros in LDS, and those rows are never
-    // stored.  Every access stays inside the operands by construction.
-    const i32x4_t rsrc_a = make_rsrc((const char*)a.A + row0 * a.lda * ASZ, (uint32_t)((int64_t)rows * a.lda * ASZ));
-    const i32x4_t rsrc_b = make_rsrc((const char*)a.B + (int64_t)g * a.b_gstride * BSZ + (int64_t)n0 * a.ldb * BSZ,
-                                     (uint32_t)((int64_t)BN * a.ldb * BSZ));
-    uint32_t a_off[A_LOADS], b_off[B_LOADS];
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int q = i * NT + tid;
-      const int r = q / CA, s = q % CA;
-      a_off[i] = (uint32_t)(r * a.lda * ASZ + (s ^ swz<CA>(r)) * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const int q = i * NT + tid;
-      const int r = q / CB, s = q % CB;
-      b_off[i] = (uint32_t)(r * a.ldb * BSZ + (s ^ swz<CB>(r)) * 16);
-    }
-    // copy l of a stage: the A chunks first, then the B chunks
-    auto issue_one = [&](int kt, int slot, int l) {
-      char* sa = smem + slot * STAGE_BYTES;
-      char* sb = sa + A_BYTES;
-      if (l < A_LOADS)
-        buffer_load_lds_16(rsrc_a, sa + (l * NT + wave * 64) * 16, a_off[l], (uint32_t)((kt0 + kt) * BK * ASZ));
-      else
-        buffer_load_lds_16<B_AUX>(rsrc_b, sb + ((l - A_LOADS) * NT + wave * 64) * 16, b_off[l - A_LOADS],
-                           (uint32_t)((kt0 + kt) * BK * BSZ));
-    };
-    auto issue = [&](int kt, int slot) {
-#pragma unroll
-      for (int l = 0; l < LOADS; ++l) issue_one(kt, slot, l);
-    };
+  // One tile.  The LDS slots form one ring across the workgroup's tiles:
+  // stage kt of this tile lives in slot (base + kt) % STAGES.  pre: stages
+  // 0 .. STAGES-2 are already in flight (issued by the previous tile); pf:
+  // the last STAGES-1 stages of this tile refill their freed slots with
+  // stages 0 .. STAGES-2 of `nit`, so the next tile's loads fly during this
+  // tile's last stages and its epilogue instead of after them.  pf requires
+  // KT >= STAGES here and >= STAGES-1 k-tiles in `nit`: then exactly
+  // STAGES-2 stages are always issued after the one a k-step waits for.
+  auto run_tile = [&](const Item& it, int base, bool pre, bool pf, const Item& nit) {
+    const int64_t row0 = it.row0;
+    const int n0 = it.n0, g = it.g, rows = it.rows;
+    float* const part = it.part;
 
     // Fragment reads go through inline-asm ds_read so that the compiler does
     // not insert its own (conservative) LDS waits: the k-step whose MFMAs
@@ -481,11 +523,18 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     // stage kt+1 visible (its first k-step is prefetched across the stage
     // boundary) and proves every wave has finished reading stage kt, whose
     // slot is then refilled with stage kt+STAGES.
-    const int KT = kt1 - kt0;
+    const int KT = it.kt1 - it.kt0;
+    auto slot_of = [&](int kt) { return (base + kt) % STAGES; };
     __syncthreads();  // every wave is done with the previous tile's LDS
+    if (pre) {
+      if (STAGES - 1 < KT) issue(it, STAGES - 1, slot_of(STAGES - 1));
+    } else {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s)
-      if (s < KT) issue(s, s);
+      for (int s = 0; s < STAGES; ++s)
+        if (s < KT) issue(it, s, slot_of(s));
+    }
+    // stage 0 has landed (anything issued after it counts too: the wait
+    // only gets stricter)
     if (KT >= STAGES) wait_vmcnt<(STAGES - 1) * LOADS>();
     else wait_vmcnt<0>();
     barrier_lds();
@@ -493,12 +542,12 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     // k-step pair (fp8).  Buffer parities of a stage's k-step 0 come in as
     // compile-time tags (stages are unrolled by two).
     frag_t fa[2][FM], fb[2][FN];
-    read_a(0, 0, fa[0]);
-    read_b(0, 0, fb[0]);
+    read_a(slot_of(0), 0, fa[0]);
+    read_b(slot_of(0), 0, fb[0]);
 
     auto stage = [&](int kt, auto pa_tag, auto pb_tag) {
       constexpr int pa = decltype(pa_tag)::value, pb = decltype(pb_tag)::value;
-      const int slot = kt % STAGES;
+      const int slot = slot_of(kt);
       const bool more = kt + 1 < KT;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -513,12 +562,13 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
           if (nb) wait_lgkmcnt<RD * (FM + FN)>();  // k-step ks has landed; the next may be in flight
           else wait_lgkmcnt<RD * FM>();
         } else if (more) {
-          if (kt + STAGES - 1 < KT) wait_vmcnt<(STAGES - 2) * LOADS>();
+          if (kt + STAGES - 1 < KT || pf) wait_vmcnt<(STAGES - 2) * LOADS>();
           else wait_vmcnt<0>();
           barrier_lds();
-          if (kt + STAGES < KT) issue(kt + STAGES, slot);
-          read_a((kt + 1) % STAGES, 0, fa[anxt]);
-          read_b((kt + 1) % STAGES, 0, fb[bnxt]);
+          if (kt + STAGES < KT) issue(it, kt + STAGES, slot);
+          else if (pf) issue(nit, kt + STAGES - KT, slot);  // the next tile's stage, into the freed slot
+          read_a(slot_of(kt + 1), 0, fa[anxt]);
+          read_b(slot_of(kt + 1), 0, fb[bnxt]);
           wait_lgkmcnt<RD * (FM + FN)>();
         } else {
           wait_lgkmcnt<0>();
@@ -562,23 +612,19 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC, false, A8>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
   };
 
-  // whole tiles of the full rounds, then (with a split) this workgroup's
-  // slice of a tail tile; one call site keeps the tile body inlined once
-  const int64_t loop_end = tp.split ? tp.full_end : tp.t_hi;
-  const bool has_slice = tp.split && xj < tp.tail * tp.split;
-  for (int64_t L = tp.t_lo + xj;; L += nx) {
-    int kt0 = 0, kt1 = KT_ALL;
-    float* part = nullptr;
-    int64_t Lt = L;
-    if (L >= loop_end) {
-      if (!has_slice || L - nx >= loop_end) break;  // the slice comes once, right after the last whole tile
-      const int tau = xj / tp.split, sig = xj % tp.split;
-      Lt = tp.full_end + tau;
-      kt0 = KT_ALL * sig / tp.split;
-      kt1 = KT_ALL * (sig + 1) / tp.split;
-      part = a.partial + (size_t)blockIdx.x * (BM * BN);
-    }
-    run_tile(Lt, kt0, kt1, part);
+  // one call site keeps the tile body inlined once
+  int64_t L = tp.t_lo + xj;
+  Item cur, nit;
+  bool have = next_item(L, cur), pre = false;
+  int base = 0;
+  while (have) {
+    const bool has_next = next_item(L, nit);
+    const bool pf = has_next && cur.kt1 - cur.kt0 >= STAGES && nit.kt1 - nit.kt0 >= STAGES - 1;
+    run_tile(cur, base, pre, pf, nit);
+    base = (base + cur.kt1 - cur.kt0) % STAGES;
+    pre = pf;
+    cur = nit;
+    have = has_next;
   }
 }
 
