@@ -103,6 +103,34 @@ def test_router_logits_within_error_bound(name):
         assert routing_mismatch_is_near_tie(cfg, ov, ref.astype(np.float32), bound, t), t
 
 
+@pytest.mark.parametrize("S,d,E,act", [(1, 4096, 8, "bf16"), (3, 704, 32, "bf16"), (2047, 4096, 8, "bf16"),
+                                       (2048, 4096, 8, "bf16"), (2049, 704, 32, "bf16"), (5, 128, 8, "f32"),
+                                       (2047, 192, 48, "f32"), (2049, 128, 8, "f32")])
+def test_fused_router_both_row_splits(S, d, E, act):
+    """The vector-ALU router splits a token's row over four waves below 2048
+    tokens and gives each token one wave from 2048 on (the last block then
+    partly past the batch).  Both forms, with rows that are not a whole
+    number of 16-byte-per-lane spans and 48 fp32 experts (two passes over
+    the row): scores within the rounding bound of the oracle's, and the
+    selection and gates exact given those scores."""
+    cfg = D.MoEConfig("r", S=S, d=d, d_ff=64, E=E, K=2, act=act, w=act, router_offset="normal",
+                      offset_beta=0.5)
+    print(f"fused router S={S} d={d} E={E} {act}", flush=True)
+    x, wr = D.tokens(cfg, DEV), D.router_weight(cfg, DEV)
+    rb = D.router_bias(cfg)
+    p = problem(cfg)
+    lo = torch.empty((S, E), dtype=torch.float32, device=DEV)
+    idx, gate = M.moe_route(p, x, wr, rb.to(DEV), None, logits_out=lo)
+    sync()
+    ov = {"x": raw(x), "W_r": raw(wr), "router_bias": rb.numpy(), "select_bias": None}
+    ref = oracle_logits(cfg, ov).astype(np.float64)
+    got = lo.cpu().numpy()
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= logit_bound(cfg, ov, ref) + 1e-30)
+    o_idx = O.select_experts(got, cfg.K)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    np.testing.assert_allclose(gate.cpu().numpy(), O.gate_weights(got, o_idx, 1), rtol=0, atol=GATE_TOL)
+
+
 # ------------------------------------------------------------------ permute
 def _permute_case(E, K, idx, d=64, act="bf16"):
     S = idx.shape[0]
