@@ -766,9 +766,15 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& a, const f32x16_t (&
 // tile's first stage the same way, so those loads fly during the epilogue.
 // Rows of a partly filled tile do all MFMAs (their loads read zeros); only
 // the stores skip them.
+// Row tiles per band of the four-wave kernel's tile order.  The up product
+// (many channel tiles) gains from taller bands: each band re-reads the
+// weights of its experts once, and 8 row tiles halve those passes (measured
+// 1-2 % on expert_up at the Mixtral and Zipf shapes; no gain on down).
+constexpr int w4_band(int epi) { return epi == EPI_GELU ? 8 : 4; }
+
 template <int EPI>
 __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const GemmArgs a) {
-  constexpr int BM = 256, BN = 256, BK = 64, NT = 256, GM = 4, MF = 32;
+  constexpr int BM = 256, BN = 256, BK = 64, NT = 256, GM = w4_band(EPI), MF = 32;
   constexpr int CA = BK * 2 / 16;  // 16-byte chunks per row
   constexpr int A_BYTES = BM * BK * 2, STAGE_BYTES = A_BYTES + BN * BK * 2;
   constexpr int A_LOADS = BM * CA / NT, B_LOADS = BN * CA / NT, LOADS = A_LOADS + B_LOADS;
@@ -1141,7 +1147,7 @@ hipError_t run_bf16_w4(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t part
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partial == nullptr) return e;
   // the fixup's thread layout matches: 2 x 2 waves of 128 x 128, 32 x 32 MFMAs
-  hipLaunchKernelGGL((grouped_gemm_fixup_kernel<256, 256, 64, 2, 2, 2, false, EPI, 4, 32>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((grouped_gemm_fixup_kernel<256, 256, 64, 2, 2, 2, false, EPI, w4_band(EPI), 32>), dim3((unsigned)grid),
                      dim3(256), 0, st, a);
   return hipGetLastError();
 }
