@@ -105,7 +105,7 @@ def test_router_logits_within_error_bound(name):
 
 @pytest.mark.parametrize("S,d,E,act", [(1, 4096, 8, "bf16"), (3, 704, 32, "bf16"), (2047, 4096, 8, "bf16"),
                                        (2048, 4096, 8, "bf16"), (2049, 704, 32, "bf16"), (5, 128, 8, "f32"),
-                                       (2047, 192, 48, "f32"), (2049, 128, 8, "f32")])
+                                       (2047, 192, 48, "f32"), (2049, 128, 8, "f32"), (2051, 192, 48, "f32")])
 def test_fused_router_both_row_splits(S, d, E, act):
     """The vector-ALU router splits a token's row over four waves below 2048
     tokens and gives each token one wave from 2048 on (the last block then
