@@ -1004,6 +1004,61 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
   }
 }
 
+// Second pass of the four-wave kernel's tail split, one single-wave
+// workgroup per 128 x 128 block of a tail tile: the reduction is bound by
+// load latency, so spreading a tile's four blocks over four compute units
+// shortens it.  Workgroup xcd + 8 (4 tau + q) takes block q (wave q of the
+// GEMM, wm = q / 2, wn = q % 2) of tail tile tau: it reads exactly the sums
+// that wave wrote, adds the slices in slice order and runs the same
+// epilogue, so the output is that of a whole-tile fixup.
+template <int EPI>
+__global__ void __launch_bounds__(64) grouped_gemm_w4_fixup_kernel(const GemmArgs a) {
+  constexpr int BM = 256, BN = 256, NT = 256, MF = 32, FM = 4, FN = 4, NACC = 16;
+  constexpr int NQ = FM * FN * NACC / 4, QB = 16;  // 16-byte groups per thread, per batch
+  const int lane = threadIdx.x;
+  const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3, tau = r >> 2, q = r & 3;
+  const int nx = (a.grid - xcd + 7) >> 3;
+  if (a.partial == nullptr || a.K / 64 < 16) return;
+  const int m_used = rows_tiles_used<BM>(a);
+  const TailPlan tp = tail_plan((int64_t)m_used * a.n_tiles, xcd, nx, true);
+  if (tp.split == 0 || tau >= tp.tail) return;
+  int64_t row0;
+  int n0, g, rows;
+  if (!tile_coords<BM, BN, w4_band(EPI)>(a, m_used, tp.full_end + tau, row0, n0, g, rows)) return;
+  const int wm = q >> 1, wn = q & 1;
+  if (wm * 128 >= rows) return;  // block wholly past the rows: nothing to store
+  const int tid = q * 64 + lane;  // the GEMM thread whose sums these are
+  float4 sum[NQ];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) sum[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q0 = 0; q0 < NQ; q0 += QB) {
+    for (int sig = 0; sig < tp.split; ++sig) {
+      const float* part = a.partial + (size_t)(xcd + 8 * (tau * tp.split + sig)) * (BM * BN);
+      float4 t[QB];
+#pragma unroll
+      for (int k = 0; k < QB; ++k) t[k] = *(const float4*)(part + ((size_t)(q0 + k) * NT + tid) * 4);
+#pragma unroll
+      for (int k = 0; k < QB; ++k) {
+        sum[q0 + k].x += t[k].x; sum[q0 + k].y += t[k].y;
+        sum[q0 + k].z += t[k].z; sum[q0 + k].w += t[k].w;
+      }
+    }
+  }
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < NACC / 4; ++v) {
+        const float4 u = sum[(i * FN + j) * (NACC / 4) + v];
+        acc[i][j][4 * v] = u.x; acc[i][j][4 * v + 1] = u.y; acc[i][j][4 * v + 2] = u.z; acc[i][j][4 * v + 3] = u.w;
+      }
+  gemm_epilogue<BN, 2, 2, false, EPI, MF, FM, FN, NACC, false, false>(a, acc, g, rows, row0, n0, wm, wn, lane % MF,
+                                                                       lane / MF);
+}
+
 // fp32 activations and weights: vector-ALU tiles (64 x 64 outputs, 4 x 4 per
 // thread), exact fp32 fused multiply-adds.
 template <int EPI>
@@ -1146,9 +1201,8 @@ hipError_t run_bf16_w4(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t part
   hipLaunchKernelGGL(grouped_gemm_bf16_w4_kernel<EPI>, dim3((unsigned)grid), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partial == nullptr) return e;
-  // the fixup's thread layout matches: 2 x 2 waves of 128 x 128, 32 x 32 MFMAs
-  hipLaunchKernelGGL((grouped_gemm_fixup_kernel<256, 256, 64, 2, 2, 2, false, EPI, w4_band(EPI), 32>), dim3((unsigned)grid),
-                     dim3(256), 0, st, a);
+  // the fixup: four single-wave workgroups per possible tail tile
+  hipLaunchKernelGGL(grouped_gemm_w4_fixup_kernel<EPI>, dim3((unsigned)grid * 4), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
