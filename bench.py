@@ -480,7 +480,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(json.dumps({"metric": METRIC, "error": "this build runs on exactly one GPU; "
+        print(json.dumps({"metric": METRIC, "error": "this MoE layer runs on exactly one GPU; "
                           f"--gpus {a.gpus} (WORLD_SIZE {world}) is not supported"}))
         sys.exit(2)
     import torch
