@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only launch a 1 GiB copy and the expert GEMMs (for rocprofv3 --pmc passes)")
+    ap.add_argument("--pmc-mfma-summary", metavar="DIR",
+                    help="write profiles/mfma_*.md from a rocprofv3 --pmc pass over the MFMA counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_*.md from two rocprofv3 --pmc output directories")
     return ap.parse_args()
@@ -254,6 +256,74 @@ def pmc_summary(a):
             f.write(f"- bytes_per_launch: {int(round(fb + wb))}\n")
             f.write(f"- fetch_bytes: {int(round(fb))}\n")
             f.write(f"- write_bytes: {int(round(wb))}\n")
+            f.write(f"- source_hash: {gemm_source_hash()}\n")
+        log(f"[bench] wrote {path}")
+
+
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE"  # one pass
+
+
+def pmc_mfma_summary(a):
+    """Turn one rocprofv3 --pmc pass over MFMA_COUNTERS (csv output) into
+    profiles/mfma_<stage>_<workload>.md: per expert GEMM dispatch, the MFMA
+    busy fraction of all SIMDs, the shader clock, and the bf16 MFMA work
+    executed (padding rows included) against the algorithmic work."""
+    import csv
+    import statistics
+
+    rows = []
+    for root, _, files in os.walk(a.pmc_mfma_summary):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                rows += list(csv.DictReader(open(os.path.join(root, f))))
+    disp = {}
+    for r in rows:
+        k = r["Kernel_Name"]
+        if "grouped_gemm_bf16" not in k or "fixup" in k:
+            continue
+        d = disp.setdefault((k, r["Dispatch_Id"]), {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    cfg_name = a.workload
+    import datagen as D
+    cfg = D.CONFIGS[cfg_name]
+    alg = 2.0 * cfg.S * cfg.K * cfg.d * cfg.d_ff
+    cus, simds, xccs = 256, 4, 8
+    for stage, epi in (("expert_up", "0"), ("expert_down", "1")):
+        ds = [v for (k, _), v in disp.items()
+              if [x.strip() for x in k.split("<", 1)[1].split(">", 1)[0].split(",")][0 if "_w4_kernel" in k else 7] == epi]
+        if not ds:
+            continue
+        kname = next(k for (k, _) in disp if k.split("<", 1)[1].split(">", 1)[0].split(",")[0 if "_w4_kernel" in k else 7].strip() == epi)
+        med = lambda f: statistics.median(f(d) for d in ds)
+        gui = med(lambda d: d["GRBM_GUI_ACTIVE"] / xccs)          # shader cycles of the dispatch
+        ghz = med(lambda d: d["GRBM_GUI_ACTIVE"] / xccs / d["ns"])
+        busy = med(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / xccs * cus * simds))
+        flops = med(lambda d: d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512)
+        ms = med(lambda d: d["ns"]) / 1e6
+        path = os.path.join(ROOT, "profiles", f"mfma_{stage}_{cfg_name}.md")
+        with open(path, "w") as f:
+            f.write(f"# MFMA utilisation: `{stage}` GEMM, {cfg_name} workload\n\n")
+            f.write("Commands (one MI355X, repository root; one counter pass, then this summary):\n\n```\n")
+            f.write(f"rocprofv3 --pmc {MFMA_COUNTERS} -d gpurun_out/pmc_mfma -o m --output-format csv -- "
+                    f"python -u bench.py --pmc-probe --workload {cfg_name}\n")
+            f.write(f"python bench.py --workload {cfg_name} --pmc-mfma-summary gpurun_out/pmc_mfma\n```\n\n")
+            f.write(f"Kernel: `{kname}` ({len(ds)} dispatches, medians).  Counters are summed over the {xccs} XCCs "
+                    f"and their SIMDs; shader cycles = GRBM_GUI_ACTIVE / {xccs}.\n\n")
+            f.write("| quantity | value |\n|:--|--:|\n")
+            f.write(f"| dispatch duration under counter collection | {ms:.3f} ms |\n")
+            f.write(f"| shader clock (cycles / duration) | {ghz:.2f} GHz |\n")
+            f.write(f"| MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {cus} CUs x {simds} SIMDs) | {100 * busy:.1f} % |\n")
+            f.write(f"| bf16 MFMA work executed: 512 SQ_INSTS_VALU_MFMA_MOPS_BF16 | {flops:.4g} flop |\n")
+            f.write(f"| algorithmic work (2 d d_ff per routed row) | {alg:.4g} flop |\n")
+            f.write(f"| executed / algorithmic (padding rows of partly filled tiles) | {flops / alg:.3f} |\n")
+            f.write(f"| executed rate during the dispatch | {flops / (ms / 1e3) / 1e12:.0f} TFLOP/s |\n")
+            f.write(f"| dense bf16 peak at the measured clock ({ghz:.2f} / 2.4 x 2.5 PFLOP/s) | "
+                    f"{2500 * ghz / 2.4:.0f} TFLOP/s |\n\n")
+            f.write("The fraction of the 2.5 PFLOP/s peak that the algorithmic work reaches factors as MFMA busy x "
+                    "(clock / 2.4 GHz) / (executed / algorithmic): "
+                    f"{busy:.3f} x {ghz / 2.4:.3f} / {flops / alg:.3f} = {busy * ghz / 2.4 / (flops / alg):.3f} under "
+                    "counter collection (the bench line's figure comes from uninstrumented launches, at a clock "
+                    "that varies from box to box).\n\n")
             f.write(f"- source_hash: {gemm_source_hash()}\n")
         log(f"[bench] wrote {path}")
 
@@ -477,6 +547,9 @@ def main():
     a = parse()
     if a.pmc_summary:
         pmc_summary(a)
+        return
+    if a.pmc_mfma_summary:
+        pmc_mfma_summary(a)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
