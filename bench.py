@@ -372,6 +372,23 @@ def run_workload(name, steps, warmup, D, M, torch):
     return cfg, w, ms, stage_ms, touched, counts
 
 
+def graph_leg(w, torch, steps, warmup):
+    """The layer captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: the same launches without the host's per-launch cost.  A
+    separate figure, never the headline."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        w.layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w.layer()
+    ms = time_calls(torch, g.replay, steps, warmup)
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.cfg.S / (ms / 1e3), 1)}
+
+
 def capacity_leg(w, M, torch, factor, steps):
     """The workload with each expert limited to factor * S*K/E pairs: the
     layer step with the limit, and moe_apply_capacity alone on the routed
@@ -593,7 +610,8 @@ def main():
         out["decode"] = {"workload": "decode", "tokens_per_s": round(dcfg.S / (dms / 1e3), 1),
                          "ms_per_step": round(dms, 4), "roofline": roofline(dcfg, dstage, dtouched, "decode"),
                          "layer": layer_fractions(dcfg, dms, dtouched, "bf16"),
-                         "stage_ms": {k: round(v, 4) for k, v in dstage.items()}}
+                         "stage_ms": {k: round(v, 4) for k, v in dstage.items()},
+                         "graph": graph_leg(dw, torch, max(a.steps, 100), a.warmup)}
         del dw
     if not a.no_skew and cfg.name != "zipf_skew":
         zcfg, zw, zms, zstage, ztouched, zcounts = run_workload("zipf_skew", a.steps, a.warmup, D, M, torch)
