@@ -9,7 +9,7 @@ import torch
 
 import datagen as D
 import sparse_ffn_layer_amd as M
-from tests.gpu_common import DEV, gpu_inputs, problem
+from tests.gpu_common import DEV, gpu_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -18,12 +18,18 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "decode", "mixtral_prefill"])
-def test_layer_graph_replays_match_eager(name):
+@pytest.mark.parametrize("name,capacity,act_quant", [("tiny_f32", 0, 0), ("decode", 0, 0), ("mixtral_prefill", 0, 0),
+                                                     ("mixtral_prefill", 1280, 0), ("zipf_skew", 600, 0),
+                                                     ("dsv3_fp8", 0, 1)])
+def test_layer_graph_replays_match_eager(name, capacity, act_quant):
+    """Also with a per-expert capacity (its rounds keep counters in the
+    workspace, reset by the kernels themselves) and with fp8 activations
+    (rows quantised between the products)."""
     cfg = D.CONFIGS[name]
     inp = gpu_inputs(name)
-    p = problem(cfg)
-    print(f"graph replay {name}", flush=True)
+    p = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                       cfg.renormalize, 1.0, capacity, act_quant)
+    print(f"graph replay {name} capacity={capacity} act_quant={act_quant}", flush=True)
     ws = M.workspace(p, M.STAGE_LAYER, DEV)
     act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
     y_eager = torch.empty((cfg.S, cfg.d), dtype=act, device=DEV)
