@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--no-capacity", action="store_true")
     ap.add_argument("--no-w8a8", action="store_true")
     ap.add_argument("--no-skew", action="store_true")
+    ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only launch a 1 GiB copy and the expert GEMMs (for rocprofv3 --pmc passes)")
@@ -372,6 +373,46 @@ def run_workload(name, steps, warmup, D, M, torch):
     return cfg, w, ms, stage_ms, touched, counts
 
 
+def context_leg(w, torch, counts):
+    """Context for the roofline, on the same box in the same run (never the
+    measured figure): a plain 1 GiB device copy, and the vendor library's
+    GEMM (torch.matmul -> hipBLASLt) on the expert-up work of the workload --
+    once as one dense product over all routed rows, once as one product per
+    expert at the routed counts, the library's way to run the same grouped
+    work."""
+    c = w.cfg
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    copy_ms = time_calls(torch, lambda: dst.copy_(src), 10, 3)
+    del src, dst
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    rows = int(sum(int(n) for n in counts))
+    # weights in the layout the expert products read them, [d_ff][d] (a
+    # linear layer's [out][in]); a plain 2-D product with the transposed view
+    a = torch.randn((rows, c.d), device="cuda", generator=gen).to(torch.bfloat16)
+    wt = torch.randn((c.d_ff, c.d), device="cuda", generator=gen).to(torch.bfloat16)
+    dense_ms = time_calls(torch, lambda: torch.mm(a, wt.t()), 10, 3)
+    ws = [torch.randn((c.d_ff, c.d), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(c.E)]
+    offs = [0]
+    for n in counts:
+        offs.append(offs[-1] + int(n))
+
+    def per_expert():
+        for e in range(c.E):
+            if offs[e + 1] > offs[e]:
+                torch.mm(a[offs[e]:offs[e + 1]], ws[e].t())
+
+    grouped_ms = time_calls(torch, per_expert, 10, 3)
+    fl = 2.0 * rows * c.d * c.d_ff
+    out = {"copy_GBps_read_plus_write": round(2 * COPY_PROBE_BYTES / (copy_ms / 1e3) / 1e9, 1),
+           "hipblaslt_dense_up_TFLOPs": round(fl / (dense_ms / 1e3) / 1e12, 1),
+           "hipblaslt_per_expert_up_TFLOPs": round(fl / (grouped_ms / 1e3) / 1e12, 1),
+           "rows": rows, "shape": f"[{rows} x {c.d}] x [{c.d} x {c.d_ff}] bf16"}
+    del a, wt, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def graph_leg(w, torch, steps, warmup):
     """The layer captured once in a HIP graph (torch.cuda.CUDAGraph) and
     replayed: the same launches without the host's per-launch cost.  A
@@ -599,6 +640,11 @@ def main():
         "layer_tflops": round(4.0 * cfg.S * cfg.K * cfg.d * cfg.d_ff / (ms / 1e3) / 1e12, 2),
     }
     log(f"[bench] {cfg.name}: {ms:.3f} ms/step, stages {out['stage_ms']}")
+    if not a.no_context and cfg.act == "bf16":
+        out["context"] = context_leg(w, torch, counts.tolist())
+        out["context"]["this_up_TFLOPs"] = out["roofline"]["achieved"] if out["roofline"]["kernel"] == "expert_up" \
+            else None
+        log(f"[bench] context: {out['context']}")
     if not a.no_capacity:
         out["capacity"] = capacity_leg(w, M, torch, 1.25, a.steps)
         log(f"[bench] capacity: {out['capacity']}")
