@@ -1,5 +1,6 @@
-// Router: scores, (group-limited) Top-K selection and gates, one wavefront
-// per token.
+// Router: scores, (group-limited) Top-K selection and gates; one wavefront
+// selects for each token (its scores summed by one wave, or by four for a
+// small batch).
 //
 // Chapter "大模型推理技术 | 第11章 MoE模型推理" (jsqmd.com), sections
 // 11.1.1-11.1.2: router scores are x W_r, a softmax over the experts gives the
