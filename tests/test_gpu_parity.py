@@ -378,6 +378,16 @@ def test_layer_edge_cases(kw):
     _layer_case(cfg, inp, np.arange(cfg.S))
 
 
+def test_layer_large_batch():
+    """40000 tokens (not a multiple of any tile): large router and combine
+    grids, a many-block dispatch and the prefill GEMMs over 80000 routed
+    rows; 40 sampled tokens, the last one included, against the oracle."""
+    cfg = D.MoEConfig("large", S=40000, d=1024, d_ff=1024, E=8, K=2, router_offset="normal", offset_beta=0.5)
+    print("large batch S=40000", flush=True)
+    inp = D.make_inputs(cfg, DEV)
+    _layer_case(cfg, inp, sample_tokens(cfg.S, 40, seed=3))
+
+
 def test_empty_batch_noop():
     cfg = D.CONFIGS["tiny_f32"]
     p = problem(cfg, S=0)
