@@ -100,7 +100,8 @@ typedef enum {
  *    bf16 activations and return MOE_ERR_UNSUPPORTED when it is set.
  *    0 = activations in act_dtype; other values: MOE_ERR_INVALID_ARG.
  *  - Limits: 1 <= E <= 512, 1 <= K <= min(E, 64), d and d_ff multiples of 64,
- *    S < 2^31 / K.  Outside them: MOE_ERR_UNSUPPORTED. */
+ *    S < 2^24 and S * K < 2^26 (every kernel launch stays below 2^32
+ *    work-items).  Outside them: MOE_ERR_UNSUPPORTED. */
 typedef struct {
   int64_t S;
   int32_t d;
@@ -259,7 +260,8 @@ int32_t moe_load_stats(const moe_problem* p, const int32_t* expert_counts, const
  * each quotient and product one float32 operation; the row's value is
  * decode(code) * scale.  A row of zeros gets scale 0 and codes 0.
  *   codes [rows][n] uint8 and scales [rows] float32 are written.
- *   n: a positive multiple of 8; rows >= 0 (0 is a no-op), < 2^31.
+ *   n: a positive multiple of 8; rows >= 0 (0 is a no-op), < 2^26 (else
+ *   MOE_ERR_UNSUPPORTED).
  * Needs no workspace and no moe_problem. */
 int32_t moe_quantize_rows(const void* src, int64_t rows, int32_t n, uint8_t* codes, float* scales,
                           void* stream);

@@ -108,6 +108,32 @@ def _stream(stream) -> Optional[int]:
     return getattr(stream, "cuda_stream", stream) or None
 
 
+def _side(stream):
+    """The launch stream as a torch stream when it is not the current one, else None.
+
+    Tensors a wrapper allocates come from torch's caching allocator on the
+    current stream.  When the kernels run on another stream, such a tensor is
+    marked as in use there (record_stream), so that freeing it when the
+    wrapper returns cannot hand its bytes to a later allocation on the current
+    stream while the launched kernels still read or write them."""
+    if stream is None:
+        return None
+    cur = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return None if stream.cuda_stream == cur.cuda_stream else stream
+    h = int(getattr(stream, "cuda_stream", stream) or 0)
+    if h == cur.cuda_stream:
+        return None
+    return torch.cuda.ExternalStream(h) if h else torch.cuda.default_stream()
+
+
+def _empty(shape, dtype, device, side):
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if side is not None:
+        t.record_stream(side)
+    return t
+
+
 def _check(fn: str, status: int):
     if status != MOE_OK:
         raise MoEError(fn, status)
@@ -129,9 +155,12 @@ def moe_rows_capacity(p: moe_problem) -> int:
     return int(lib().moe_rows_capacity(ctypes.byref(p)))
 
 
-def workspace(p: moe_problem, stage: int, device="cuda") -> torch.Tensor:
+def workspace(p: moe_problem, stage: int, device="cuda", side=None) -> torch.Tensor:
+    """Workspace of entry point `stage` for p; `side`: the stream the kernels
+    run on when it is not the current one (the tensor is then marked as in
+    use there)."""
     n = moe_workspace_bytes(p, stage)
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return _empty(max(n, 1), torch.uint8, device, side)
 
 
 def _act(p: moe_problem):
@@ -142,12 +171,13 @@ def _act(p: moe_problem):
 def moe_route(p, x, W_r, router_bias=None, select_bias=None, logits_in=None, logits_out=None,
               topk_idx=None, topk_gate=None, ws=None, stream=None):
     dev = (logits_in if logits_in is not None else x).device
+    side = _side(stream)
     if topk_idx is None:
-        topk_idx = torch.empty((p.S, p.K), dtype=torch.int32, device=dev)
+        topk_idx = _empty((p.S, p.K), torch.int32, dev, side)
     if topk_gate is None:
-        topk_gate = torch.empty((p.S, p.K), dtype=torch.float32, device=dev)
+        topk_gate = _empty((p.S, p.K), torch.float32, dev, side)
     if ws is None:
-        ws = workspace(p, STAGE_ROUTE, dev)
+        ws = workspace(p, STAGE_ROUTE, dev, side)
     st = lib().moe_route(ctypes.byref(p), _ptr(x), _ptr(W_r), _ptr(router_bias), _ptr(select_bias),
                          _ptr(logits_in), _ptr(logits_out), _ptr(topk_idx), _ptr(topk_gate),
                          _ptr(ws), ws.numel(), _stream(stream))
@@ -158,16 +188,16 @@ def moe_route(p, x, W_r, router_bias=None, select_bias=None, logits_in=None, log
 def moe_permute(p, topk_idx, x, expert_counts=None, expert_offsets=None, perm=None, inv_perm=None,
                 x_perm=None, ws=None, stream=None):
     dev = topk_idx.device
+    side = _side(stream)
     pairs = p.S * p.K
-    i32 = dict(dtype=torch.int32, device=dev)
-    expert_counts = torch.empty(p.E, **i32) if expert_counts is None else expert_counts
-    expert_offsets = torch.empty(p.E + 1, **i32) if expert_offsets is None else expert_offsets
-    perm = torch.empty(pairs, **i32) if perm is None else perm
-    inv_perm = torch.empty(pairs, **i32) if inv_perm is None else inv_perm
+    expert_counts = _empty(p.E, torch.int32, dev, side) if expert_counts is None else expert_counts
+    expert_offsets = _empty(p.E + 1, torch.int32, dev, side) if expert_offsets is None else expert_offsets
+    perm = _empty(pairs, torch.int32, dev, side) if perm is None else perm
+    inv_perm = _empty(pairs, torch.int32, dev, side) if inv_perm is None else inv_perm
     if x_perm is None:
-        x_perm = torch.empty((moe_rows_capacity(p), p.d), dtype=_act(p), device=dev)
+        x_perm = _empty((moe_rows_capacity(p), p.d), _act(p), dev, side)
     if ws is None:
-        ws = workspace(p, STAGE_PERMUTE, dev)
+        ws = workspace(p, STAGE_PERMUTE, dev, side)
     st = lib().moe_permute(ctypes.byref(p), _ptr(topk_idx), _ptr(x), _ptr(expert_counts),
                            _ptr(expert_offsets), _ptr(perm), _ptr(inv_perm), _ptr(x_perm),
                            _ptr(ws), ws.numel(), _stream(stream))
@@ -178,11 +208,12 @@ def moe_permute(p, topk_idx, x, expert_counts=None, expert_offsets=None, perm=No
 def moe_expert_ffn(p, x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, w1_scale=None,
                    w2_scale=None, h=None, y_perm=None, ws=None, stream=None):
     dev = x_perm.device
+    side = _side(stream)
     cap = moe_rows_capacity(p)
-    h = torch.empty((cap, p.d_ff), dtype=_act(p), device=dev) if h is None else h
-    y_perm = torch.empty((cap, p.d), dtype=_act(p), device=dev) if y_perm is None else y_perm
+    h = _empty((cap, p.d_ff), _act(p), dev, side) if h is None else h
+    y_perm = _empty((cap, p.d), _act(p), dev, side) if y_perm is None else y_perm
     if ws is None:
-        ws = workspace(p, STAGE_EXPERT_FFN, dev)
+        ws = workspace(p, STAGE_EXPERT_FFN, dev, side)
     st = lib().moe_expert_ffn(ctypes.byref(p), _ptr(x_perm), _ptr(expert_counts), _ptr(expert_offsets),
                               _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(w1_scale), _ptr(w2_scale),
                               _ptr(h), _ptr(y_perm), _ptr(ws), ws.numel(), _stream(stream))
@@ -192,10 +223,11 @@ def moe_expert_ffn(p, x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, w1_
 
 def moe_expert_up(p, x_perm, expert_counts, expert_offsets, W1, b1, w1_scale=None, h=None, ws=None,
                   stream=None):
+    side = _side(stream)
     if h is None:
-        h = torch.empty((moe_rows_capacity(p), p.d_ff), dtype=_act(p), device=x_perm.device)
+        h = _empty((moe_rows_capacity(p), p.d_ff), _act(p), x_perm.device, side)
     if ws is None:
-        ws = workspace(p, STAGE_EXPERT_FFN, x_perm.device)
+        ws = workspace(p, STAGE_EXPERT_FFN, x_perm.device, side)
     st = lib().moe_expert_up(ctypes.byref(p), _ptr(x_perm), _ptr(expert_counts), _ptr(expert_offsets),
                              _ptr(W1), _ptr(b1), _ptr(w1_scale), _ptr(h), _ptr(ws), ws.numel(),
                              _stream(stream))
@@ -205,10 +237,11 @@ def moe_expert_up(p, x_perm, expert_counts, expert_offsets, W1, b1, w1_scale=Non
 
 def moe_expert_down(p, h, expert_counts, expert_offsets, W2, b2, w2_scale=None, y_perm=None, ws=None,
                     stream=None):
+    side = _side(stream)
     if y_perm is None:
-        y_perm = torch.empty((moe_rows_capacity(p), p.d), dtype=_act(p), device=h.device)
+        y_perm = _empty((moe_rows_capacity(p), p.d), _act(p), h.device, side)
     if ws is None:
-        ws = workspace(p, STAGE_EXPERT_FFN, h.device)
+        ws = workspace(p, STAGE_EXPERT_FFN, h.device, side)
     st = lib().moe_expert_down(ctypes.byref(p), _ptr(h), _ptr(expert_counts), _ptr(expert_offsets),
                                _ptr(W2), _ptr(b2), _ptr(w2_scale), _ptr(y_perm), _ptr(ws), ws.numel(),
                                _stream(stream))
@@ -218,7 +251,7 @@ def moe_expert_down(p, h, expert_counts, expert_offsets, W2, b2, w2_scale=None, 
 
 def moe_combine(p, y_perm, inv_perm, topk_gate, y=None, stream=None):
     if y is None:
-        y = torch.empty((p.S, p.d), dtype=_act(p), device=y_perm.device)
+        y = _empty((p.S, p.d), _act(p), y_perm.device, _side(stream))
     st = lib().moe_combine(ctypes.byref(p), _ptr(y_perm), _ptr(inv_perm), _ptr(topk_gate), _ptr(y),
                            _stream(stream))
     _check("moe_combine", st)
@@ -228,10 +261,11 @@ def moe_combine(p, y_perm, inv_perm, topk_gate, y=None, stream=None):
 def moe_layer_forward(p, x, W_r, W1, b1, W2, b2, router_bias=None, select_bias=None, w1_scale=None,
                       w2_scale=None, y=None, topk_idx_out=None, topk_gate_out=None, logits_out=None,
                       expert_counts_out=None, ws=None, stream=None):
+    side = _side(stream)
     if y is None:
-        y = torch.empty((p.S, p.d), dtype=_act(p), device=x.device)
+        y = _empty((p.S, p.d), _act(p), x.device, side)
     if ws is None:
-        ws = workspace(p, STAGE_LAYER, x.device)
+        ws = workspace(p, STAGE_LAYER, x.device, side)
     st = lib().moe_layer_forward(ctypes.byref(p), _ptr(x), _ptr(W_r), _ptr(router_bias),
                                  _ptr(select_bias), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
                                  _ptr(w1_scale), _ptr(w2_scale), _ptr(y), _ptr(topk_idx_out),
@@ -245,7 +279,9 @@ def moe_load_stats(p, expert_counts, logits=None, dropped=None, alpha=1.0, stats
     """Load statistics of one routing as a float32 tensor [MOE_STATS_N] on the
     device, in the order of STAT_NAMES (see moe_load_stats in include/moe.h)."""
     if stats is None:
-        stats = torch.zeros(MOE_STATS_N, dtype=torch.float32, device=expert_counts.device)
+        # every entry is written by the kernel: no fill on the current stream
+        # that could race with a launch on another one
+        stats = _empty(MOE_STATS_N, torch.float32, expert_counts.device, _side(stream))
     st = lib().moe_load_stats(ctypes.byref(p), _ptr(expert_counts), _ptr(logits), _ptr(dropped),
                               float(alpha), _ptr(stats), _stream(stream))
     _check("moe_load_stats", st)
@@ -256,12 +292,13 @@ def moe_apply_capacity(p, logits, topk_idx, select_bias=None, topk_gate=None, dr
                        stream=None):
     """Capacity-limited dispatch with p.capacity pairs per expert; topk_idx
     is updated in place.  Returns (topk_idx, topk_gate, dropped[1])."""
+    side = _side(stream)
     if topk_gate is None:
-        topk_gate = torch.empty((p.S, p.K), dtype=torch.float32, device=topk_idx.device)
+        topk_gate = _empty((p.S, p.K), torch.float32, topk_idx.device, side)
     if dropped is None:
-        dropped = torch.zeros(4, dtype=torch.int32, device=topk_idx.device)
+        dropped = _empty(4, torch.int32, topk_idx.device, side)  # entry 0 is written by the kernel
     if ws is None:
-        ws = workspace(p, STAGE_CAPACITY, topk_idx.device)
+        ws = workspace(p, STAGE_CAPACITY, topk_idx.device, side)
     st = lib().moe_apply_capacity(ctypes.byref(p), _ptr(logits), _ptr(select_bias), _ptr(topk_idx),
                                   _ptr(topk_gate), _ptr(dropped), _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_apply_capacity", st)
@@ -272,10 +309,11 @@ def moe_quantize_rows(src, codes=None, scales=None, stream=None):
     """Per-row e4m3 quantisation of a bf16 matrix [rows, n]: returns (codes
     uint8 [rows, n], scales float32 [rows])."""
     rows, n = src.shape
+    side = _side(stream)
     if codes is None:
-        codes = torch.empty((rows, n), dtype=torch.uint8, device=src.device)
+        codes = _empty((rows, n), torch.uint8, src.device, side)
     if scales is None:
-        scales = torch.empty(max(rows, 1), dtype=torch.float32, device=src.device)
+        scales = _empty(max(rows, 1), torch.float32, src.device, side)
     st = lib().moe_quantize_rows(_ptr(src), int(rows), int(n), _ptr(codes), _ptr(scales), _stream(stream))
     _check("moe_quantize_rows", st)
     return codes, scales[:rows]

@@ -45,6 +45,8 @@ using namespace sfl;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxTokens = int64_t(1) << 24;  // S < 2^24
+constexpr int64_t kMaxPairs = int64_t(1) << 26;   // S * K < 2^26
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -76,7 +78,9 @@ int32_t check_problem(const moe_problem* mp, Problem* out) {
                      (q.act_dtype == MOE_BF16 && (q.w_dtype == MOE_BF16 || q.w_dtype == MOE_FP8_E4M3));
   if (!combo) return MOE_ERR_UNSUPPORTED;
   if (q.E > 512 || q.K > 64 || q.d % 64 != 0 || q.d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  if (q.S > 0 && q.S >= (int64_t)(INT32_MAX / 2) / q.K) return MOE_ERR_UNSUPPORTED;
+  // every launch stays below 2^32 work-items: the combine takes 256 threads
+  // per token, the row gather and the row quantiser 64 per (token, slot) pair
+  if (q.S >= kMaxTokens || q.S * q.K >= kMaxPairs) return MOE_ERR_UNSUPPORTED;
   // fp8 activations: bf16 activations and fp8 weights, k a multiple of 128
   if (q.act_quant && (q.act_dtype != MOE_BF16 || q.w_dtype != MOE_FP8_E4M3 || q.d % 128 != 0 ||
                       q.d_ff % 128 != 0))
@@ -345,7 +349,7 @@ int32_t moe_quantize_rows(const void* src, int64_t rows, int32_t n, uint8_t* cod
                           void* stream) {
   if (rows < 0 || n < 8 || n % 8 != 0) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
-  if (rows > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (rows >= kMaxPairs) return MOE_ERR_UNSUPPORTED;  // 64 threads per row, < 2^32 in all
   for (const void* q : {(const void*)src, (const void*)codes, (const void*)scales})
     if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_quantize_rows((const uint16_t*)src, n, n, rows, 1, false, nullptr, codes, n, scales,

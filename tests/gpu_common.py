@@ -88,3 +88,56 @@ def near_tie(keys_row, K, gap):
     """True if the K-th and (K+1)-th largest keys are within `gap`."""
     s = np.sort(np.asarray(keys_row, dtype=np.float64))[::-1]
     return K < len(s) and (s[K - 1] - s[K]) <= gap
+
+
+def split_tail_tiles(offsets, rows_cap, N, K, BM, BN, BK, GM, grid=256):
+    """Tiles whose k range the grouped GEMM splits: the host-side replica of
+    its persistent schedule.  The tile space (row tiles in use x N / BN
+    channel tiles, in bands of GM row tiles, the row tile fastest) is cut into
+    8 contiguous slices, one per XCD; each slice runs in rounds of its
+    grid / 8 workgroups, and when its last round is partial with at least
+    twice as many idle workgroups as tail tiles and K / BK >= 16 k-tiles,
+    the tail tiles run split along k.  `grid` is the launch's workgroup
+    count (256: one workgroup per compute unit of an MI355X for the 128-row
+    tiles).  Returns [(row0, n0, expert)] of the split tiles."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = len(offsets) - 1
+    m_tiles = -(-rows_cap // BM)
+    m_used = min(-(-int(offsets[E]) // BM), m_tiles)
+    n_tiles = N // BN
+    T = m_used * n_tiles
+    g = min(grid, m_tiles * n_tiles)
+    g = 8 if g < 8 else g // 8 * 8
+    if K // BK < 16:
+        return []
+    out = []
+    for xcd in range(8):
+        nx = (g - xcd + 7) >> 3
+        t_lo, t_hi = T * xcd // 8, T * (xcd + 1) // 8
+        tx = t_hi - t_lo
+        full_end = t_lo + tx // nx * nx
+        tail = tx % nx
+        split = nx // tail if tail else 0
+        if split < 2:
+            continue
+        for tau in range(tail):
+            L = full_end + tau
+            band = GM * n_tiles
+            bnd = L // band
+            first_m = bnd * GM
+            gm = min(m_used - first_m, GM)
+            rem = L - bnd * band
+            mt, nt = first_m + rem % gm, rem // gm
+            row0 = mt * BM
+            if row0 >= offsets[E]:
+                continue
+            e = int(np.searchsorted(offsets, row0, side="right") - 1)
+            out.append((row0, nt * BN, e))
+    return out
+
+
+def host_x_perm(cfg, xr, pm, cap):
+    """x_perm built on the host from the oracle's permutation (padding rows 0)."""
+    xp = np.zeros((cap, cfg.d), dtype=xr.dtype)
+    xp[pm["inv_perm"]] = xr[np.arange(cfg.S * cfg.K) // cfg.K]
+    return xp

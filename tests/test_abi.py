@@ -107,6 +107,25 @@ def test_invalid_problems_rejected(kw, status):
     assert lib.moe_apply_capacity(ctypes.byref(p), *([fake] * 5), fake, 1 << 40, None) == status
 
 
+@pytest.mark.parametrize("S,K,ok", [((1 << 24) - 1, 2, True), (1 << 24, 2, False), ((1 << 24) - 1, 4, True),
+                                    ((1 << 24) - 1, 8, False), ((1 << 23), 8, False), ((1 << 23) - 1, 8, True),
+                                    ((1 << 20), 64, False), ((1 << 20) - 1, 64, True)])
+def test_token_and_pair_limits(S, K, ok):
+    """S < 2^24 and S * K < 2^26: every kernel launch stays below 2^32
+    work-items (256 threads per token in the combine, 64 per pair in the row
+    gather and quantiser)."""
+    p = prob(S=S, K=K, E=64)
+    lib = M.lib()
+    assert (lib.moe_tile_m(ctypes.byref(p)) > 0) == ok
+    assert (lib.moe_rows_capacity(ctypes.byref(p)) > 0) == ok
+    if not ok:
+        fake = ctypes.c_void_p(1 << 20)
+        assert lib.moe_layer_forward(ctypes.byref(p), *([fake] * 15), fake, 1 << 62, None) == M.MOE_ERR_UNSUPPORTED
+    q = lib.moe_quantize_rows
+    fake = ctypes.c_void_p(1 << 20)
+    assert q(fake, 1 << 26, 64, fake, fake, None) == M.MOE_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("tau,ok", [(0.0, True), (1.0, True), (0.25, True), (-1.0, False),
                                     (float("nan"), False), (float("inf"), False)])
 def test_gate_temperature_validation(tau, ok):

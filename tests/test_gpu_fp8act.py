@@ -11,7 +11,7 @@ import datagen as D
 import oracle as O
 import sparse_ffn_layer_amd as M
 from tests._util import raw
-from tests.gpu_common import DEV, TOL, gpu_inputs, oracle_view, sample_tokens
+from tests.gpu_common import DEV, GATE_TOL, TOL, gpu_inputs, oracle_view, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -76,9 +76,10 @@ def _layer_w8a8(cfg, inp, tokens, cap=0):
                        cfg.renormalize, 1.0, cap, 1)
     logits = torch.empty((cfg.S, cfg.E), dtype=torch.float32, device=DEV)
     idx = torch.empty((cfg.S, cfg.K), dtype=torch.int32, device=DEV)
+    gate = torch.empty((cfg.S, cfg.K), dtype=torch.float32, device=DEV)
     y = M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
                             inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"],
-                            topk_idx_out=idx, logits_out=logits)
+                            topk_idx_out=idx, topk_gate_out=gate, logits_out=logits)
     sync()
     ov = oracle_view(inp)
     lg = logits.cpu().numpy()
@@ -88,7 +89,12 @@ def _layer_w8a8(cfg, inp, tokens, cap=0):
     ref = O.layer_forward(ov["x"], ov["W_r"], ov["W1"], ov["b1"], ov["W2"], ov["b2"], K=cfg.K, act=cfg.act,
                           w=cfg.w, select_bias=ov["select_bias"], n_groups=cfg.n_groups,
                           topk_groups=cfg.topk_groups, renormalize=cfg.renormalize, w1_scale=ov["w1_scale"],
-                          w2_scale=ov["w2_scale"], logits_in=lg, tokens=tokens, capacity=cap, act_quant=True)
+                          w2_scale=ov["w2_scale"], logits_in=lg, tokens=tokens, capacity=cap, act_quant=True,
+                          return_parts=True)
+    # routing from the GPU's own scores: indices exact, gates to GATE_TOL
+    assert np.array_equal(idx.cpu().numpy()[tokens], ref["idx"])
+    np.testing.assert_allclose(gate.cpu().numpy()[tokens], ref["gates"], rtol=0, atol=GATE_TOL)
+    ref = ref["y"]
     yg = O.decode(raw(y[torch.from_numpy(np.asarray(tokens)).to(DEV)]), cfg.act)
     err = np.abs(yg - ref).max() / np.abs(ref).max()
     print(f"w8a8 {cfg.name} S={cfg.S} rel err {err:.3e}", flush=True)

@@ -329,6 +329,10 @@ def _layer_case(cfg, inp, tokens):
         bound = logit_bound(cfg, ov, ref_logits.astype(np.float64))
         for t in np.nonzero(~same_all)[0]:
             assert routing_mismatch_is_near_tie(cfg, ov, ref_logits, bound, t), t
+    # the oracle's gates come from its own scores, which differ from the GPU's
+    # by the float32 rounding of the router product (up to ~1e-6 relative at
+    # d = 7168), so the gates are compared at 1e-5 here; tests that route from
+    # the GPU's own scores hold them to GATE_TOL
     np.testing.assert_allclose(gate_out.cpu().numpy()[same_all], o_gate[same_all], atol=1e-5, rtol=0)
     # the oracle's whole forward on the sampled tokens
     ref = O.layer_forward(ov["x"], ov["W_r"], ov["W1"], ov["b1"], ov["W2"], ov["b2"], K=cfg.K,
@@ -347,7 +351,7 @@ def _layer_case(cfg, inp, tokens):
     return y
 
 
-SAMPLE = {"tiny_f32": 64, "mixtral_prefill": 48, "decode": 16, "zipf_skew": 48, "dsv3_fp8": 8}
+SAMPLE = {"tiny_f32": 64, "mixtral_prefill": 48, "decode": 16, "zipf_skew": 48, "dsv3_fp8": 64}
 
 
 @pytest.mark.parametrize("name", ALL)
