@@ -60,7 +60,9 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1, /* bad shape, NULL or misaligned pointer, bad flag */
   MOE_ERR_UNSUPPORTED = -2, /* valid problem outside what the kernels handle */
   MOE_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than required */
-  MOE_ERR_HIP = -4          /* a HIP launch failed */
+  MOE_ERR_HIP = -4,         /* a HIP launch failed */
+  MOE_ERR_TOO_LARGE = -5    /* moe_layer_forward_noalloc: the problem needs more
+                               than MOE_NOALLOC_SCRATCH_BYTES of workspace */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -312,6 +314,37 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x, const void* W_r,
                           int32_t* topk_idx_out, float* topk_gate_out,
                           float* logits_out, int32_t* expert_counts_out,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the library's own scratch array (one per GPU), the workspace of
+ * moe_layer_forward_noalloc: 128 MiB. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* moe_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, meaning and results as moe_layer_forward
+ * (bit-identical outputs for the same inputs), without ws / ws_bytes: the
+ * workspace is a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends.
+ *  - Problems with moe_workspace_bytes(p, MOE_STAGE_LAYER) above
+ *    MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_TOO_LARGE before anything is
+ *    launched (this covers decode-sized batches: e.g. up to 255 tokens at
+ *    d = 4096, d_ff = 14336, E = 8, K = 2, or 16 tokens at d = 7168,
+ *    d_ff = 2048, E = 256, K = 8).  Other validation as moe_layer_forward.
+ *  - The call allocates nothing: no hipMalloc, hipFree or allocating
+ *    library routine.  The first call on a GPU looks up that GPU's copy of
+ *    the array (hipGetSymbolAddress, on the stream's device) and keeps the
+ *    address; make that first call outside graph capture.
+ *  - Every call on one GPU uses the same array, which keeps the last call's
+ *    contents (no kernel of the layer depends on them: each initialises the
+ *    state it reads).  Calls that overlap on one GPU -- concurrent streams,
+ *    or replays of several captured graphs at once -- race on it; order them
+ *    on one stream or use moe_layer_forward with separate workspaces. */
+int32_t moe_layer_forward_noalloc(const moe_problem* p, const void* x, const void* W_r,
+                                  const float* router_bias, const float* select_bias,
+                                  const void* W1, const void* b1, const void* W2, const void* b2,
+                                  const float* w1_scale, const float* w2_scale, void* y,
+                                  int32_t* topk_idx_out, float* topk_gate_out,
+                                  float* logits_out, int32_t* expert_counts_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,11 +19,14 @@ __all__ = [
     "STAGE_COMBINE", "STAGE_LAYER", "MoEError", "moe_problem", "make_problem", "lib", "LIB_PATH",
     "moe_workspace_bytes", "moe_tile_m", "moe_rows_capacity", "moe_status_string",
     "workspace", "moe_load_stats", "moe_apply_capacity", "moe_quantize_rows", "STAGE_CAPACITY", "MOE_STATS_N", "STAT_NAMES", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
+    "moe_layer_forward_noalloc", "MOE_ERR_TOO_LARGE", "MOE_NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfl_moe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_TOO_LARGE = -5
+MOE_NOALLOC_SCRATCH_BYTES = 128 << 20   # the library's own scratch array per GPU (moe.h)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 STAGE_ROUTE, STAGE_PERMUTE, STAGE_EXPERT_FFN, STAGE_COMBINE, STAGE_LAYER, STAGE_CAPACITY = 0, 1, 2, 3, 4, 5
 # moe_load_stats outputs, in order (MOE_STAT_* in include/moe.h)
@@ -72,6 +75,7 @@ _SIGS = {
     "moe_expert_down": (_i32, [_P] + [_vp] * 7 + [_vp, _sz, _vp]),
     "moe_combine": (_i32, [_P] + [_vp] * 4 + [_vp]),
     "moe_layer_forward": (_i32, [_P] + [_vp] * 15 + [_vp, _sz, _vp]),
+    "moe_layer_forward_noalloc": (_i32, [_P] + [_vp] * 15 + [_vp]),
     "moe_load_stats": (_i32, [_P, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "moe_apply_capacity": (_i32, [_P] + [_vp] * 5 + [_vp, _sz, _vp]),
     "moe_quantize_rows": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
@@ -272,6 +276,20 @@ def moe_layer_forward(p, x, W_r, W1, b1, W2, b2, router_bias=None, select_bias=N
                                  _ptr(topk_gate_out), _ptr(logits_out), _ptr(expert_counts_out),
                                  _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_layer_forward", st)
+    return y
+
+
+def moe_layer_forward_noalloc(p, x, W_r, W1, b1, W2, b2, y, router_bias=None, select_bias=None,
+                              w1_scale=None, w2_scale=None, topk_idx_out=None, topk_gate_out=None,
+                              logits_out=None, expert_counts_out=None, stream=None):
+    """moe_layer_forward on the library's own scratch array: the caller passes
+    every input and output (y included) and nothing is allocated."""
+    st = lib().moe_layer_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(W_r), _ptr(router_bias),
+                                         _ptr(select_bias), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                                         _ptr(w1_scale), _ptr(w2_scale), _ptr(y), _ptr(topk_idx_out),
+                                         _ptr(topk_gate_out), _ptr(logits_out), _ptr(expert_counts_out),
+                                         _stream(stream))
+    _check("moe_layer_forward_noalloc", st)
     return y
 
 

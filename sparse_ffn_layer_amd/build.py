@@ -21,7 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsfl_moe.so")
-SOURCES = ["api.cpp", "router.hip", "capacity.hip", "permute.hip", "quant.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "noalloc.hip", "router.hip", "capacity.hip", "permute.hip", "quant.hip", "gemm.hip",
+           "combine.hip"]
 ARCH = "gfx950"
 
 

@@ -9,6 +9,7 @@
 #include <initializer_list>
 
 #include "common.h"
+#include "layer.h"
 
 namespace sfl {
 // kernels (router.hip, capacity.hip, permute.hip, quant.hip, gemm.hip, combine.hip)
@@ -204,6 +205,75 @@ int32_t do_route(const Problem& p, const void* x, const void* Wr, const float* r
 
 }  // namespace
 
+namespace sfl {
+
+int32_t layer_validate(const moe_problem* mp, const LayerArgs& a, size_t* need) {
+  *need = 0;
+  Problem p;
+  int32_t s = check_problem(mp, &p);
+  if (s != MOE_OK) return s;
+  if (p.S == 0) return MOE_OK;
+  const void* req[] = {a.x, a.W_r, a.W1, a.b1, a.W2, a.b2, a.y};
+  for (const void* q : req)
+    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  const void* opt[] = {a.router_bias, a.select_bias, a.w1_scale, a.w2_scale, a.topk_idx_out,
+                       a.topk_gate_out, a.logits_out, a.expert_counts_out};
+  for (const void* q : opt)
+    if (!aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (p.w == DT_FP8 && (a.w1_scale == nullptr || a.w2_scale == nullptr)) return MOE_ERR_INVALID_ARG;
+  *need = layer_layout(p, nullptr).bytes;
+  return MOE_OK;
+}
+
+int32_t layer_run(const moe_problem* mp, const LayerArgs& a, void* ws, hipStream_t st) {
+  Problem p;
+  int32_t s = check_problem(mp, &p);
+  if (s != MOE_OK) return s;
+  const LayerWs w = layer_layout(p, (char*)ws);
+  int32_t* idx = a.topk_idx_out != nullptr ? a.topk_idx_out : w.idx;
+  float* gate = a.topk_gate_out != nullptr ? a.topk_gate_out : w.gate;
+  int32_t* counts = a.expert_counts_out != nullptr ? a.expert_counts_out : w.counts;
+  // the capacity step reads the scores again, so they are kept in that case
+  float* lg = (p.capacity > 0 && a.logits_out == nullptr) ? w.logits : a.logits_out;
+  s = do_route(p, a.x, a.W_r, a.router_bias, a.select_bias, nullptr, lg, idx, gate, w.logits, st);
+  if (s != MOE_OK) return s;
+  if (p.capacity > 0) {
+    s = hip_status(launch_capacity(p, p.capacity, lg, a.select_bias, idx, gate, nullptr, w.cscratch, st));
+    if (s != MOE_OK) return s;
+  }
+  if (p.act_quant) {
+    // W8A8: the gather writes e4m3 rows and row scales; h is quantised per
+    // row between the two products
+    const int64_t pairs = p.S * p.K, cap = rows_capacity(p);
+    uint8_t* x8 = (uint8_t*)w.x_perm;
+    s = hip_status(launch_permute(p, gemm_tile_m(p), idx, a.x, counts, w.offsets, w.perm, w.inv, nullptr,
+                                  w.pscratch, st));
+    if (s != MOE_OK) return s;
+    s = hip_status(launch_quantize_rows((const uint16_t*)a.x, p.d, p.d, pairs, p.K, true, w.inv, x8, p.d, w.xs,
+                                        st));
+    if (s != MOE_OK) return s;
+    s = hip_status(launch_expert_up(p, cap, x8, counts, w.offsets, a.W1, a.b1, a.w1_scale, w.h, w.split,
+                                    w.split_bytes, st, w.xs));
+    if (s != MOE_OK) return s;
+    s = hip_status(launch_quantize_rows((const uint16_t*)w.h, p.d_ff, p.d_ff, pairs, p.K, false, w.inv, w.h8,
+                                        p.d_ff, w.hs, st));
+    if (s != MOE_OK) return s;
+    s = hip_status(launch_expert_down(p, cap, w.h8, counts, w.offsets, a.W2, a.b2, a.w2_scale, w.y_perm,
+                                      w.split, w.split_bytes, st, w.hs));
+    if (s != MOE_OK) return s;
+    return hip_status(launch_combine(p, w.y_perm, w.inv, gate, a.y, st));
+  }
+  s = hip_status(launch_permute(p, gemm_tile_m(p), idx, a.x, counts, w.offsets, w.perm, w.inv,
+                                w.x_perm, w.pscratch, st));
+  if (s != MOE_OK) return s;
+  s = do_expert_ffn(p, w.x_perm, counts, w.offsets, a.W1, a.b1, a.W2, a.b2, a.w1_scale, a.w2_scale, w.h,
+                    w.y_perm, w.split, w.split_bytes, st);
+  if (s != MOE_OK) return s;
+  return hip_status(launch_combine(p, w.y_perm, w.inv, gate, a.y, st));
+}
+
+}  // namespace sfl
+
 extern "C" {
 
 const char* moe_status_string(int32_t s) {
@@ -213,6 +283,7 @@ const char* moe_status_string(int32_t s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported problem";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_TOO_LARGE: return "problem needs more workspace than the no-alloc scratch array holds";
     default: return "unknown status";
   }
 }
@@ -377,62 +448,13 @@ int32_t moe_layer_forward(const moe_problem* mp, const void* x, const void* W_r,
                           const float* w2_scale, void* y, int32_t* topk_idx_out,
                           float* topk_gate_out, float* logits_out, int32_t* expert_counts_out,
                           void* ws, size_t ws_bytes, void* stream) {
-  Problem p;
-  int32_t s = check_problem(mp, &p);
-  if (s != MOE_OK) return s;
-  if (p.S == 0) return MOE_OK;
-  const void* req[] = {x, W_r, W1, b1, W2, b2, y};
-  for (const void* q : req)
-    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
-  const void* opt[] = {router_bias, select_bias, w1_scale, w2_scale, topk_idx_out, topk_gate_out,
-                       logits_out, expert_counts_out};
-  for (const void* q : opt)
-    if (!aligned16(q)) return MOE_ERR_INVALID_ARG;
-  if (p.w == DT_FP8 && (w1_scale == nullptr || w2_scale == nullptr)) return MOE_ERR_INVALID_ARG;
-  const LayerWs need = layer_layout(p, nullptr);
-  if (ws == nullptr || ws_bytes < need.bytes) return MOE_ERR_WORKSPACE;
-
-  const LayerWs w = layer_layout(p, (char*)ws);
-  hipStream_t st = (hipStream_t)stream;
-  int32_t* idx = topk_idx_out != nullptr ? topk_idx_out : w.idx;
-  float* gate = topk_gate_out != nullptr ? topk_gate_out : w.gate;
-  int32_t* counts = expert_counts_out != nullptr ? expert_counts_out : w.counts;
-  // the capacity step reads the scores again, so they are kept in that case
-  float* lg = (p.capacity > 0 && logits_out == nullptr) ? w.logits : logits_out;
-  s = do_route(p, x, W_r, router_bias, select_bias, nullptr, lg, idx, gate, w.logits, st);
-  if (s != MOE_OK) return s;
-  if (p.capacity > 0) {
-    s = hip_status(launch_capacity(p, p.capacity, lg, select_bias, idx, gate, nullptr, w.cscratch, st));
-    if (s != MOE_OK) return s;
-  }
-  if (p.act_quant) {
-    // W8A8: the gather writes e4m3 rows and row scales; h is quantised per
-    // row between the two products
-    const int64_t pairs = p.S * p.K, cap = rows_capacity(p);
-    uint8_t* x8 = (uint8_t*)w.x_perm;
-    s = hip_status(launch_permute(p, gemm_tile_m(p), idx, x, counts, w.offsets, w.perm, w.inv, nullptr,
-                                  w.pscratch, st));
-    if (s != MOE_OK) return s;
-    s = hip_status(launch_quantize_rows((const uint16_t*)x, p.d, p.d, pairs, p.K, true, w.inv, x8, p.d, w.xs, st));
-    if (s != MOE_OK) return s;
-    s = hip_status(launch_expert_up(p, cap, x8, counts, w.offsets, W1, b1, w1_scale, w.h, w.split,
-                                    w.split_bytes, st, w.xs));
-    if (s != MOE_OK) return s;
-    s = hip_status(launch_quantize_rows((const uint16_t*)w.h, p.d_ff, p.d_ff, pairs, p.K, false, w.inv, w.h8,
-                                        p.d_ff, w.hs, st));
-    if (s != MOE_OK) return s;
-    s = hip_status(launch_expert_down(p, cap, w.h8, counts, w.offsets, W2, b2, w2_scale, w.y_perm, w.split,
-                                      w.split_bytes, st, w.hs));
-    if (s != MOE_OK) return s;
-    return hip_status(launch_combine(p, w.y_perm, w.inv, gate, y, st));
-  }
-  s = hip_status(launch_permute(p, gemm_tile_m(p), idx, x, counts, w.offsets, w.perm, w.inv,
-                                w.x_perm, w.pscratch, st));
-  if (s != MOE_OK) return s;
-  s = do_expert_ffn(p, w.x_perm, counts, w.offsets, W1, b1, W2, b2, w1_scale, w2_scale, w.h,
-                    w.y_perm, w.split, w.split_bytes, st);
-  if (s != MOE_OK) return s;
-  return hip_status(launch_combine(p, w.y_perm, w.inv, gate, y, st));
+  const LayerArgs a{x, W_r, router_bias, select_bias, W1, b1, W2, b2, w1_scale, w2_scale, y,
+                    topk_idx_out, topk_gate_out, logits_out, expert_counts_out};
+  size_t need = 0;
+  int32_t s = layer_validate(mp, a, &need);
+  if (s != MOE_OK || need == 0) return s;
+  if (ws == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return layer_run(mp, a, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -105,6 +105,7 @@ def test_invalid_problems_rejected(kw, status):
     assert lib.moe_expert_up(ctypes.byref(p), *([fake] * 7), None, 0, None) == status
     assert lib.moe_expert_down(ctypes.byref(p), *([fake] * 7), None, 0, None) == status
     assert lib.moe_apply_capacity(ctypes.byref(p), *([fake] * 5), fake, 1 << 40, None) == status
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(p), *args15, None) == status
 
 
 @pytest.mark.parametrize("S,K,ok", [((1 << 24) - 1, 2, True), (1 << 24, 2, False), ((1 << 24) - 1, 4, True),
@@ -124,6 +125,27 @@ def test_token_and_pair_limits(S, K, ok):
     q = lib.moe_quantize_rows
     fake = ctypes.c_void_p(1 << 20)
     assert q(fake, 1 << 26, 64, fake, fake, None) == M.MOE_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_problems_past_its_scratch():
+    """moe_layer_forward_noalloc checks the layer's workspace against its
+    scratch array on the host, before any HIP call: a problem that needs more
+    returns MOE_ERR_TOO_LARGE; pointer checks come first; S == 0 is a no-op."""
+    lib = M.lib()
+    a = ctypes.c_void_p(1 << 20)
+    base = [a, a, None, None, a, a, a, a, None, None, a, None, None, None, None]
+    big = prob(S=4096, d=4096, d_ff=14336, E=8, K=2)
+    assert M.moe_workspace_bytes(big, M.STAGE_LAYER) > M.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(big), *base, None) == M.MOE_ERR_TOO_LARGE
+    assert "no-alloc" in M.moe_status_string(M.MOE_ERR_TOO_LARGE)
+    bad = list(base); bad[0] = None
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(big), *bad, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(prob(S=0)), *([None] * 15), None) == M.MOE_OK
+    # decode-sized problems fit: the shapes the header names
+    for kw in (dict(S=255, d=4096, d_ff=14336, E=8, K=2),
+               dict(S=16, d=7168, d_ff=2048, E=256, K=8, w="fp8", n_groups=8, topk_groups=2),
+               dict(S=16, d=7168, d_ff=2048, E=256, K=8, w="fp8", n_groups=8, topk_groups=2, act_quant=1)):
+        assert 0 < M.moe_workspace_bytes(prob(**kw), M.STAGE_LAYER) <= M.MOE_NOALLOC_SCRATCH_BYTES, kw
 
 
 @pytest.mark.parametrize("tau,ok", [(0.0, True), (1.0, True), (0.25, True), (-1.0, False),
@@ -152,7 +174,8 @@ def test_null_problem_and_status_strings():
     lib = M.lib()
     assert lib.moe_tile_m(None) == -1
     assert lib.moe_route(None, *([None] * 8), None, 0, None) == M.MOE_ERR_INVALID_ARG
-    for s, txt in ((0, "ok"), (-1, "invalid"), (-2, "unsupported"), (-3, "workspace"), (-4, "HIP")):
+    for s, txt in ((0, "ok"), (-1, "invalid"), (-2, "unsupported"), (-3, "workspace"), (-4, "HIP"),
+                   (-5, "scratch")):
         assert txt in M.moe_status_string(s)
 
 
