@@ -3,20 +3,24 @@
 One step = one moe_layer_forward (route, permute, expert up/down GEMMs,
 combine) over the workload's S tokens, inputs resident in HBM.  Prints ONE
 JSON line on stdout: MoE-layer tokens/s at the Mixtral-shape prefill workload
-(S=4096, d=4096, d_ff=14336, E=8, K=2, bf16), the roofline of the dominant
-kernel, the decode workload's HBM fraction, the same layer under a
-per-expert capacity, the DeepSeek-shape fp8 layer with fp8 activations, and
-the CPU oracle's rate on a bounded sample of the same workload.
+(S=4096, d=4096, d_ff=14336, E=8, K=2, bf16; median of per-step HIP-event
+times), the roofline of the dominant kernel, and the other workloads' legs:
+the same layer under a per-expert capacity, the DeepSeek-shape fp8-weight
+layer with bf16 and with e4m3 activations (per-product rooflines), the
+decode workload's HBM fraction, the Zipf-skewed layer; and the CPU oracle's
+rate on a bounded sample of every workload.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--no-decode] [--no-capacity] [--no-w8a8]
-       python bench.py --pmc-probe [--workload NAME]     (under rocprofv3 --pmc)
+       python bench.py --pmc-probe [--workload NAME] [--act-quant]   (under rocprofv3 --pmc)
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
+       python bench.py --pmc-mfma-summary DIR [--workload NAME]
 """
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -47,6 +51,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only launch a 1 GiB copy and the expert GEMMs (for rocprofv3 --pmc passes)")
+    ap.add_argument("--act-quant", action="store_true",
+                    help="with --pmc-probe: the fp8-activation (W8A8) products of the workload")
     ap.add_argument("--pmc-mfma-summary", metavar="DIR",
                     help="write profiles/mfma_*.md from a rocprofv3 --pmc pass over the MFMA counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -108,32 +114,39 @@ class Workload:
 
 
 def time_calls(torch, fn, steps, warmup):
-    """Average ms per call, HIP events on the stream the library launches on."""
+    """(mean, median) ms per call.  HIP events are recorded on the stream the
+    library launches on (torch's current stream) between back-to-back calls,
+    so each call's duration is the gap between two events and the durations
+    add up to the whole timed region."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    e.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return sum(per) / steps, statistics.median(per)
 
 
-def algorithmic(cfg, touched):
+def algorithmic(cfg, touched, a8=False):
     """Per-launch algorithmic flops and HBM bytes of the two expert GEMMs.
 
     Flops count only the S*K routed rows (no padding).  Bytes: each touched
     expert's weights (+ fp8 scales) and biases once, the routed activation
-    rows in and out once."""
+    rows in and out once (with fp8 activations, a8: e4m3 rows plus a float32
+    scale per row in, bf16 out)."""
     a = 2 if cfg.act == "bf16" else 4
+    a_in = 1 if a8 else a
+    row_sc = 4 if a8 else 0
     w = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.w]
     rows = cfg.S * cfg.K
     fl = 2.0 * rows * cfg.d * cfg.d_ff
     sc = 4 if cfg.w == "fp8" else 0
-    up = touched * (cfg.d * cfg.d_ff * w + cfg.d_ff * (a + sc)) + rows * (cfg.d + cfg.d_ff) * a
-    down = touched * (cfg.d_ff * cfg.d * w + cfg.d * (a + sc)) + rows * (cfg.d_ff + cfg.d) * a
+    up = touched * (cfg.d * cfg.d_ff * w + cfg.d_ff * (a + sc)) + rows * (cfg.d * a_in + row_sc + cfg.d_ff * a)
+    down = touched * (cfg.d_ff * cfg.d * w + cfg.d * (a + sc)) + rows * (cfg.d_ff * a_in + row_sc + cfg.d * a)
     return {"expert_up": (fl, up), "expert_down": (fl, down)}
 
 
@@ -173,7 +186,8 @@ COPY_PROBE_BYTES = 1 << 30   # plain device copy of known size: scales the HBM c
 def pmc_probe(a, D, M, torch):
     """Launch only what the counter passes need: a plain 1 GiB device copy
     (three times) and the workload's two expert GEMM stages (three times
-    each), so FETCH_SIZE / WRITE_SIZE per dispatch can be read off."""
+    each; with --act-quant the W8A8 products on rows quantised per row), so
+    the counters per dispatch can be read off."""
     cfg = D.CONFIGS[a.workload]
     src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -186,11 +200,38 @@ def pmc_probe(a, D, M, torch):
     st["route"]()
     st["permute"]()
     torch.cuda.synchronize()
-    for _ in range(3):
+    if a.act_quant:
+        i = w.inp
+        p8 = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                            cfg.renormalize, 1.0, 0, 1)
+        x8, xs = M.moe_quantize_rows(w.x_perm)
         st["expert_up"]()
-        st["expert_down"]()
+        h8, hs = M.moe_quantize_rows(w.h)
+        for _ in range(3):
+            M.moe_expert_up_a8(p8, x8, xs, w.counts, w.offsets, i["W1"], i["b1"], i["w1_scale"], h=w.h, ws=w.ws_ffn)
+            M.moe_expert_down_a8(p8, h8, hs, w.counts, w.offsets, i["W2"], i["b2"], i["w2_scale"], y_perm=w.y_perm,
+                                 ws=w.ws_ffn)
+    else:
+        for _ in range(3):
+            st["expert_up"]()
+            st["expert_down"]()
     torch.cuda.synchronize()
-    log(f"[bench] pmc probe done: {cfg.name}")
+    log(f"[bench] pmc probe done: {cfg.name}{' (W8A8)' if a.act_quant else ''}")
+
+
+def gemm_kernel_stage(k):
+    """(stage, fp8 activations?) of an expert GEMM kernel name, or None.  The
+    epilogue (0: bias + GeLU = expert_up, 1: bias = expert_down) is the only
+    template argument of the four-wave kernel and the eighth of the general
+    one, whose eleventh says whether the activations are e4m3."""
+    if "grouped_gemm_bf16" not in k or "fixup" in k or "<" not in k:
+        return None
+    args = [x.strip() for x in k.split("<", 1)[1].split(">", 1)[0].split(",")]
+    epi = args[0] if "_w4_kernel" in k else args[7]
+    if epi not in ("0", "1"):
+        return None
+    a8 = len(args) > 10 and args[10] == "true"
+    return ("expert_up" if epi == "0" else "expert_down"), a8
 
 
 def pmc_summary(a):
@@ -224,18 +265,14 @@ def pmc_summary(a):
               and max(fk[k]) * 1024 > COPY_PROBE_BYTES / 4)
     f_scale = statistics.median(sorted(fk[ck])[-3:]) * 1024 / COPY_PROBE_BYTES
     w_scale = statistics.median(sorted(wk[ck])[-3:]) * 1024 / COPY_PROBE_BYTES
-    # the expert GEMM kernels: expert_up has epilogue 0 (bias+GeLU), expert_down
-    # epilogue 1 (bias); the epilogue is the only template argument of the
-    # four-wave kernel and the eighth of the general one
     stages = {}
     for k in fk:
-        if "grouped_gemm_bf16" not in k or "fixup" in k:
-            continue
-        args = [x.strip() for x in k.split("<", 1)[1].split(">", 1)[0].split(",")]
-        epi = args[0] if "_w4_kernel" in k else args[7]
-        stages["expert_up" if epi == "0" else "expert_down"] = k
-    cfg_name = a.workload
-    for stage, k in stages.items():
+        sa = gemm_kernel_stage(k)
+        if sa is not None and len(fk[k]) >= 3:   # the probe launches each product three times
+            stages[sa] = k
+    for (stage, a8), k in stages.items():
+        cfg_name = a.workload + ("_w8a8" if a8 else "")
+        probe = " --act-quant" if a8 else ""
         fb = statistics.median(fk[k]) * 1024 / f_scale
         wb = statistics.median(wk[k]) * 1024 / w_scale
         path = traffic_path(stage, cfg_name)
@@ -243,10 +280,11 @@ def pmc_summary(a):
             f.write(f"# HBM traffic: `{stage}` GEMM, {cfg_name} workload\n\n")
             f.write("Commands (one MI355X, repository root; two counter passes, then this summary):\n\n```\n")
             f.write(f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o f --output-format csv -- "
-                    f"python -u bench.py --pmc-probe --workload {cfg_name}\n")
+                    f"python -u bench.py --pmc-probe --workload {a.workload}{probe}\n")
             f.write(f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o w --output-format csv -- "
-                    f"python -u bench.py --pmc-probe --workload {cfg_name}\n")
-            f.write(f"python bench.py --workload {cfg_name} --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write\n```\n\n")
+                    f"python -u bench.py --pmc-probe --workload {a.workload}{probe}\n")
+            f.write(f"python bench.py --workload {a.workload} --pmc-summary gpurun_out/pmc_fetch "
+                    f"gpurun_out/pmc_write\n```\n\n")
             f.write(f"Kernel: `{k}` ({len(fk[k])} dispatches, median per dispatch).\n\n")
             f.write("| counter | raw (KiB per dispatch) | plain-copy scale (counter bytes / true bytes) | HBM bytes per launch |\n")
             f.write("|:--|--:|--:|--:|\n")
@@ -262,13 +300,15 @@ def pmc_summary(a):
 
 
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE"  # one pass
+MFMA_COUNTERS_F8 = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE"
 
 
 def pmc_mfma_summary(a):
-    """Turn one rocprofv3 --pmc pass over MFMA_COUNTERS (csv output) into
+    """Turn one rocprofv3 --pmc pass over MFMA_COUNTERS (or MFMA_COUNTERS_F8
+    for the fp8-activation products; csv output) into
     profiles/mfma_<stage>_<workload>.md: per expert GEMM dispatch, the MFMA
-    busy fraction of all SIMDs, the shader clock, and the bf16 MFMA work
-    executed (padding rows included) against the algorithmic work."""
+    busy fraction of all SIMDs, the shader clock, and the MFMA work executed
+    (padding rows included) against the algorithmic work."""
     import csv
     import statistics
 
@@ -280,48 +320,55 @@ def pmc_mfma_summary(a):
     disp = {}
     for r in rows:
         k = r["Kernel_Name"]
-        if "grouped_gemm_bf16" not in k or "fixup" in k:
+        if gemm_kernel_stage(k) is None:
             continue
         d = disp.setdefault((k, r["Dispatch_Id"]), {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
-    cfg_name = a.workload
     import datagen as D
-    cfg = D.CONFIGS[cfg_name]
+    cfg = D.CONFIGS[a.workload]
     alg = 2.0 * cfg.S * cfg.K * cfg.d * cfg.d_ff
     cus, simds, xccs = 256, 4, 8
-    for stage, epi in (("expert_up", "0"), ("expert_down", "1")):
-        ds = [v for (k, _), v in disp.items()
-              if [x.strip() for x in k.split("<", 1)[1].split(">", 1)[0].split(",")][0 if "_w4_kernel" in k else 7] == epi]
-        if not ds:
+    kernels = {}
+    for (k, _), d in disp.items():
+        kernels.setdefault(k, []).append(d)
+    for k, ds in kernels.items():
+        if len(ds) < 3:
             continue
-        kname = next(k for (k, _) in disp if k.split("<", 1)[1].split(">", 1)[0].split(",")[0 if "_w4_kernel" in k else 7].strip() == epi)
+        stage, a8 = gemm_kernel_stage(k)
+        mops = next((c for c in ds[0] if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")), None)
+        if mops is None:
+            continue
+        dt = mops.rsplit("_", 1)[1].lower()
+        cfg_name = a.workload + ("_w8a8" if a8 else "")
+        counters = MFMA_COUNTERS_F8 if a8 else MFMA_COUNTERS
+        probe = " --act-quant" if a8 else ""
+        peak = PEAK_TFLOPS["fp8" if a8 else "bf16"]
         med = lambda f: statistics.median(f(d) for d in ds)
-        gui = med(lambda d: d["GRBM_GUI_ACTIVE"] / xccs)          # shader cycles of the dispatch
         ghz = med(lambda d: d["GRBM_GUI_ACTIVE"] / xccs / d["ns"])
         busy = med(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / xccs * cus * simds))
-        flops = med(lambda d: d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512)
+        flops = med(lambda d: d[mops] * 512)
         ms = med(lambda d: d["ns"]) / 1e6
         path = os.path.join(ROOT, "profiles", f"mfma_{stage}_{cfg_name}.md")
         with open(path, "w") as f:
             f.write(f"# MFMA utilisation: `{stage}` GEMM, {cfg_name} workload\n\n")
             f.write("Commands (one MI355X, repository root; one counter pass, then this summary):\n\n```\n")
-            f.write(f"rocprofv3 --pmc {MFMA_COUNTERS} -d gpurun_out/pmc_mfma -o m --output-format csv -- "
-                    f"python -u bench.py --pmc-probe --workload {cfg_name}\n")
-            f.write(f"python bench.py --workload {cfg_name} --pmc-mfma-summary gpurun_out/pmc_mfma\n```\n\n")
-            f.write(f"Kernel: `{kname}` ({len(ds)} dispatches, medians).  Counters are summed over the {xccs} XCCs "
+            f.write(f"rocprofv3 --pmc {counters} -d gpurun_out/pmc_mfma -o m --output-format csv -- "
+                    f"python -u bench.py --pmc-probe --workload {a.workload}{probe}\n")
+            f.write(f"python bench.py --workload {a.workload} --pmc-mfma-summary gpurun_out/pmc_mfma\n```\n\n")
+            f.write(f"Kernel: `{k}` ({len(ds)} dispatches, medians).  Counters are summed over the {xccs} XCCs "
                     f"and their SIMDs; shader cycles = GRBM_GUI_ACTIVE / {xccs}.\n\n")
             f.write("| quantity | value |\n|:--|--:|\n")
             f.write(f"| dispatch duration under counter collection | {ms:.3f} ms |\n")
             f.write(f"| shader clock (cycles / duration) | {ghz:.2f} GHz |\n")
             f.write(f"| MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {cus} CUs x {simds} SIMDs) | {100 * busy:.1f} % |\n")
-            f.write(f"| bf16 MFMA work executed: 512 SQ_INSTS_VALU_MFMA_MOPS_BF16 | {flops:.4g} flop |\n")
+            f.write(f"| {dt} MFMA work executed: 512 {mops} | {flops:.4g} flop |\n")
             f.write(f"| algorithmic work (2 d d_ff per routed row) | {alg:.4g} flop |\n")
             f.write(f"| executed / algorithmic (padding rows of partly filled tiles) | {flops / alg:.3f} |\n")
             f.write(f"| executed rate during the dispatch | {flops / (ms / 1e3) / 1e12:.0f} TFLOP/s |\n")
-            f.write(f"| dense bf16 peak at the measured clock ({ghz:.2f} / 2.4 x 2.5 PFLOP/s) | "
-                    f"{2500 * ghz / 2.4:.0f} TFLOP/s |\n\n")
-            f.write("The fraction of the 2.5 PFLOP/s peak that the algorithmic work reaches factors as MFMA busy x "
-                    "(clock / 2.4 GHz) / (executed / algorithmic): "
+            f.write(f"| dense {'fp8' if a8 else 'bf16'} peak at the measured clock ({ghz:.2f} / 2.4 x "
+                    f"{peak / 1000:.1f} PFLOP/s) | {peak * ghz / 2.4:.0f} TFLOP/s |\n\n")
+            f.write(f"The fraction of the {peak / 1000:.1f} PFLOP/s peak that the algorithmic work reaches factors as "
+                    "MFMA busy x (clock / 2.4 GHz) / (executed / algorithmic): "
                     f"{busy:.3f} x {ghz / 2.4:.3f} / {flops / alg:.3f} = {busy * ghz / 2.4 / (flops / alg):.3f} under "
                     "counter collection (the bench line's figure comes from uninstrumented launches, at a clock "
                     "that varies from box to box).\n\n")
@@ -329,13 +376,17 @@ def pmc_mfma_summary(a):
         log(f"[bench] wrote {path}")
 
 
-def roofline(cfg, stage_ms, touched, workload):
-    alg = algorithmic(cfg, touched)
-    name = max(("expert_up", "expert_down"), key=lambda k: stage_ms[k])
+def roofline(cfg, stage_ms, touched, workload, kernel=None, a8=False):
+    """Roofline of one expert GEMM (the slower of the two unless `kernel` is
+    named): algorithmic work per launch over its average launch duration,
+    against the dense MFMA peak of its operand type or the HBM peak,
+    whichever its arithmetic intensity makes binding."""
+    alg = algorithmic(cfg, touched, a8)
+    name = kernel or max(("expert_up", "expert_down"), key=lambda k: stage_ms[k])
     fl, by = alg[name]
     sec = stage_ms[name] / 1e3
     intensity = fl / by
-    peak_f = PEAK_TFLOPS["bf16" if cfg.act == "bf16" else "f32"]
+    peak_f = PEAK_TFLOPS["fp8" if a8 else ("bf16" if cfg.act == "bf16" else "f32")]
     ridge = peak_f * 1e12 / (PEAK_GBS * 1e9)
     if intensity >= ridge:
         ach, peak, unit, bound = fl / sec / 1e12, peak_f, "TFLOP/s", "mfma"
@@ -343,7 +394,8 @@ def roofline(cfg, stage_ms, touched, workload):
         ach, peak, unit, bound = by / sec / 1e9, PEAK_GBS, "GB/s", "hbm"
     return {"kernel": name, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
             "frac": round(ach / peak, 4), "traffic": traffic_for(name, workload),
-            "avg_launch_ms": round(stage_ms[name], 4), "algorithmic_flops": fl, "algorithmic_bytes": by}
+            "avg_launch_ms": round(stage_ms[name], 4), "algorithmic_flops": fl, "algorithmic_bytes": by,
+            "mfma_frac": round(fl / sec / (peak_f * 1e12), 4), "hbm_frac": round(by / sec / (PEAK_GBS * 1e9), 4)}
 
 
 def layer_fractions(cfg, ms, touched, mfma_dtype):
@@ -364,13 +416,19 @@ def layer_fractions(cfg, ms, touched, mfma_dtype):
 
 
 def run_workload(name, steps, warmup, D, M, torch):
+    """The layer step (mean and median ms) and each stage's mean and median
+    launch time; the expert counts of the step."""
     cfg = D.CONFIGS[name]
     w = Workload(cfg, D, M, torch)
-    ms = time_calls(torch, w.layer, steps, warmup)
+    ms, ms_med = time_calls(torch, w.layer, steps, warmup)
     counts = w.counts.cpu()
     touched = int((counts > 0).sum())
-    stage_ms = {k: time_calls(torch, fn, steps, max(2, warmup // 2)) for k, fn in w.stages().items()}
-    return cfg, w, ms, stage_ms, touched, counts
+    st = {k: time_calls(torch, fn, steps, max(2, warmup // 2)) for k, fn in w.stages().items()}
+    return cfg, w, (ms, ms_med), st, touched, counts
+
+
+def stage_dicts(st):
+    return ({k: v[0] for k, v in st.items()}, {k: round(v[1], 4) for k, v in st.items()})
 
 
 def context_leg(w, torch, counts):
@@ -383,7 +441,7 @@ def context_leg(w, torch, counts):
     c = w.cfg
     src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
-    copy_ms = time_calls(torch, lambda: dst.copy_(src), 10, 3)
+    copy_ms = time_calls(torch, lambda: dst.copy_(src), 10, 3)[0]
     del src, dst
     gen = torch.Generator(device="cuda").manual_seed(0)
     rows = int(sum(int(n) for n in counts))
@@ -391,7 +449,7 @@ def context_leg(w, torch, counts):
     # linear layer's [out][in]); a plain 2-D product with the transposed view
     a = torch.randn((rows, c.d), device="cuda", generator=gen).to(torch.bfloat16)
     wt = torch.randn((c.d_ff, c.d), device="cuda", generator=gen).to(torch.bfloat16)
-    dense_ms = time_calls(torch, lambda: torch.mm(a, wt.t()), 10, 3)
+    dense_ms = time_calls(torch, lambda: torch.mm(a, wt.t()), 10, 3)[0]
     ws = [torch.randn((c.d_ff, c.d), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(c.E)]
     offs = [0]
     for n in counts:
@@ -402,7 +460,7 @@ def context_leg(w, torch, counts):
             if offs[e + 1] > offs[e]:
                 torch.mm(a[offs[e]:offs[e + 1]], ws[e].t())
 
-    grouped_ms = time_calls(torch, per_expert, 10, 3)
+    grouped_ms = time_calls(torch, per_expert, 10, 3)[0]
     fl = 2.0 * rows * c.d * c.d_ff
     out = {"copy_GBps_read_plus_write": round(2 * COPY_PROBE_BYTES / (copy_ms / 1e3) / 1e9, 1),
            "hipblaslt_dense_up_TFLOPs": round(fl / (dense_ms / 1e3) / 1e12, 1),
@@ -426,8 +484,9 @@ def graph_leg(w, torch, steps, warmup):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         w.layer()
-    ms = time_calls(torch, g.replay, steps, warmup)
-    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.cfg.S / (ms / 1e3), 1)}
+    ms, med = time_calls(torch, g.replay, steps, warmup)
+    return {"ms_per_step": round(med, 4), "ms_per_step_mean": round(ms, 4),
+            "tokens_per_s": round(w.cfg.S / (med / 1e3), 1)}
 
 
 def capacity_leg(w, M, torch, factor, steps):
@@ -448,7 +507,7 @@ def capacity_leg(w, M, torch, factor, steps):
                             i["select_bias"], i["w1_scale"], i["w2_scale"], y=y, expert_counts_out=counts,
                             logits_out=logits, ws=ws)
 
-    layer_ms = time_calls(torch, layer, steps, 3)
+    layer_ms, layer_med = time_calls(torch, layer, steps, 3)
     M.moe_route(w.p, i["x"], i["W_r"], i["router_bias"], i["select_bias"], topk_idx=w.idx, topk_gate=w.gate,
                 ws=w.ws_route)
     idx0 = w.idx.clone()
@@ -464,98 +523,172 @@ def capacity_leg(w, M, torch, factor, steps):
         if k >= 3:
             evs.append((s, e))
     torch.cuda.synchronize()
-    apply_ms = sum(s.elapsed_time(e) for s, e in evs) / len(evs)
+    per = [s.elapsed_time(e) for s, e in evs]
     nd = int(dropped.cpu()[0])
     moved = int((w.idx != idx0).sum().cpu()) - nd
-    return {"factor": factor, "capacity": cap, "layer_ms_per_step": round(layer_ms, 4),
-            "tokens_per_s": round(c.S / (layer_ms / 1e3), 1), "apply_capacity_ms": round(apply_ms, 4),
+    return {"factor": factor, "capacity": cap, "layer_ms_per_step": round(layer_med, 4),
+            "layer_ms_per_step_mean": round(layer_ms, 4),
+            "tokens_per_s": round(c.S / (layer_med / 1e3), 1), "apply_capacity_ms": round(statistics.median(per), 4),
             "rerouted_pairs": moved, "dropped_pairs": nd, "drop_rate": round(nd / (c.S * c.K), 5)}
 
 
-def w8a8_leg(D, M, torch, steps, warmup):
-    """The DeepSeek-shape fp8-weight layer with e4m3 activations (W8A8)
-    against the same layer with bf16 activations (W8A16), same inputs.  The
-    expert products stream every touched expert's fp8 weights once, so the
-    weight bytes over the step time are reported next to the HBM peak."""
+def w8a8_leg(D, M, torch, steps, warmup, cpu_budget=0.0):
+    """The DeepSeek-shape fp8-weight layer with bf16 activations (W8A16) and
+    with e4m3 activations (W8A8), same inputs: the layer step, every stage
+    alone (the W8A8 products through moe_expert_up_a8 / moe_expert_down_a8,
+    the row quantisations through moe_quantize_rows), and the roofline of
+    each expert product.  The products stream every touched expert's fp8
+    weights once, so they are HBM-bound at their algorithmic intensity."""
     cfg = D.CONFIGS["dsv3_fp8"]
-    inp = D.make_inputs(cfg, "cuda")
-    torch.cuda.synchronize()
-    y = torch.empty((cfg.S, cfg.d), dtype=torch.bfloat16, device="cuda")
-    counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
-    out = {"workload": cfg.name}
-    for aq in (0, 1):
-        p = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
-                           cfg.renormalize, 1.0, 0, aq)
-        ws = M.workspace(p, M.STAGE_LAYER, "cuda")
+    w = Workload(cfg, D, M, torch)
+    inp, out = w.inp, {"workload": cfg.name}
+    ms16, med16 = time_calls(torch, w.layer, steps, warmup)
+    counts = w.counts.cpu()
+    touched = int((counts > 0).sum())
+    st16 = {k: time_calls(torch, fn, steps, 2) for k, fn in w.stages().items()}
+    # W8A8: the layer, then its stages one by one
+    p8 = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                        cfg.renormalize, 1.0, 0, 1)
+    ws8 = M.workspace(p8, M.STAGE_LAYER, "cuda")
+    y8 = torch.empty_like(w.y)
 
-        def step():
-            M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
-                                inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"], y=y,
-                                expert_counts_out=counts, ws=ws)
+    def layer8():
+        M.moe_layer_forward(p8, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                            inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"], y=y8,
+                            expert_counts_out=w.counts, ws=ws8)
 
-        ms = time_calls(torch, step, steps, warmup)
-        out["ms_per_step_w8a8" if aq else "ms_per_step_w8a16"] = round(ms, 4)
-        del ws
-    touched = int((counts > 0).sum().cpu())
+    ms8, med8 = time_calls(torch, layer8, steps, warmup)
+    cap = M.moe_rows_capacity(p8)
+    x8 = torch.empty((cap, cfg.d), dtype=torch.uint8, device="cuda")
+    xs = torch.empty(cap, dtype=torch.float32, device="cuda")
+    h8 = torch.empty((cap, cfg.d_ff), dtype=torch.uint8, device="cuda")
+    hs = torch.empty(cap, dtype=torch.float32, device="cuda")
+    for fn in w.stages().values():   # routing, permutation and x_perm of this step
+        fn()
+    st8 = {
+        "quantize_x": lambda: M.moe_quantize_rows(w.x_perm, x8, xs),
+        "expert_up": lambda: M.moe_expert_up_a8(p8, x8, xs, w.counts, w.offsets, inp["W1"], inp["b1"],
+                                                inp["w1_scale"], h=w.h, ws=w.ws_ffn),
+        "quantize_h": lambda: M.moe_quantize_rows(w.h, h8, hs),
+        "expert_down": lambda: M.moe_expert_down_a8(p8, h8, hs, w.counts, w.offsets, inp["W2"], inp["b2"],
+                                                    inp["w2_scale"], y_perm=w.y_perm, ws=w.ws_ffn),
+    }
+    st8 = {k: time_calls(torch, fn, steps, 2) for k, fn in st8.items()}
+    m16, d16 = stage_dicts(st16)
+    m8, d8 = stage_dicts(st8)
     wbytes = touched * 2 * cfg.d * cfg.d_ff + touched * 4 * (cfg.d + cfg.d_ff)
-    ms = out["ms_per_step_w8a8"]
-    out.update({"tokens_per_s": round(cfg.S / (ms / 1e3), 1), "experts_touched": touched,
-                "expert_weight_bytes": wbytes,
-                "weight_stream_GBps": round(wbytes / (ms / 1e3) / 1e9, 1), "hbm_peak_GBps": PEAK_GBS,
-                "layer_w8a8": layer_fractions(cfg, ms, touched, "fp8"),
-                "layer_w8a16": layer_fractions(cfg, out["ms_per_step_w8a16"], touched, "bf16")})
-    del inp
+    out.update({
+        "ms_per_step_w8a8": round(med8, 4), "ms_per_step_w8a8_mean": round(ms8, 4),
+        "ms_per_step_w8a16": round(med16, 4), "ms_per_step_w8a16_mean": round(ms16, 4),
+        "tokens_per_s": round(cfg.S / (med8 / 1e3), 1), "tokens_per_s_w8a16": round(cfg.S / (med16 / 1e3), 1),
+        "experts_touched": touched, "expert_weight_bytes": wbytes,
+        "weight_stream_GBps": round(wbytes / (med8 / 1e3) / 1e9, 1), "hbm_peak_GBps": PEAK_GBS,
+        "layer_w8a8": layer_fractions(cfg, med8, touched, "fp8"),
+        "layer_w8a16": layer_fractions(cfg, med16, touched, "bf16"),
+        "stage_ms_w8a16": {k: round(v, 4) for k, v in m16.items()}, "stage_ms_median_w8a16": d16,
+        "stage_ms_w8a8": {k: round(v, 4) for k, v in m8.items()}, "stage_ms_median_w8a8": d8,
+        "roofline_w8a16": {k: roofline(cfg, m16, touched, cfg.name, k) for k in ("expert_up", "expert_down")},
+        "roofline_w8a8": {k: roofline(cfg, m8, touched, cfg.name + "_w8a8", k, a8=True)
+                          for k in ("expert_up", "expert_down")},
+    })
+    if cpu_budget > 0:
+        out["cpu_loops"] = cpu_loops_rate(cfg, inp, cpu_budget, torch, max_experts=100)
+    del w, ws8, x8, h8
     torch.cuda.empty_cache()
     return out
 
 
-def cpu_loops_baseline(cfg, w, target_s, torch):
+# ------------------------------------------------------------------ CPU oracle
+def _host_decode(t, dt, torch, scale=None):
+    """A device tensor of storage dtype `dt` -> float64 host array (fp8 times
+    its per-output-channel scale)."""
+    import numpy as np
+
+    from oracle import cref
+    t = t.detach().cpu()
+    if dt == "bf16":
+        v = cref.decode(t.view(torch.int16).numpy().view(np.uint16), "bf16")
+    elif dt == "fp8":
+        v = cref.decode(t.view(torch.uint8).numpy(), "fp8")
+    else:
+        v = t.double().numpy()
+    if scale is not None:
+        v *= scale.detach().cpu().double().numpy()[:, None]
+    return v
+
+
+def cpu_loops_rate(cfg, inp, budget_s, torch, threads=None, n_tokens=None, repeats=1, max_experts=None):
     """The plain C++ loops of oracle/moe_oracle_ref.cpp (OpenMP over tokens,
-    double precision) on the first n tokens of the same workload; the
-    experts' weights are decoded to double before the timed call."""
+    double precision) as they stand, on the first n tokens of the workload:
+    n grows until one call costs about budget_s (or covers S, or touches more
+    than max_experts experts), unless n_tokens fixes it.  Device inputs are
+    copied and decoded to double beforehand, only for the experts the sample
+    routes to (the other experts' weights are untouched zero pages); timed is
+    the oracle_layer_forward call alone (scores, selection, gates, every
+    routed pair's expert FFN, combine).  Returns tokens/s and what ran."""
     import numpy as np
 
     from oracle import cref
     if not os.path.exists(cref.LIB_PATH):
         return None
-
-    def host(t, dt):
-        t = t.detach().cpu()
-        if t.dtype == torch.bfloat16:
-            return cref.decode(t.view(torch.int16).numpy().view(np.uint16), "bf16")
-        if t.dtype == torch.float8_e4m3fn:
-            return cref.decode(t.view(torch.uint8).numpy(), "fp8")
-        return t.double().numpy()
-
-    inp = w.inp
-    if cfg.w == "fp8":
-        return None     # the loops take the fp8 scales folded in; measured on bf16 workloads only
-    W1, W2 = host(inp["W1"], cfg.w), host(inp["W2"], cfg.w)
-    b1, b2 = host(inp["b1"], cfg.act), host(inp["b2"], cfg.act)
-    wr = host(inp["W_r"], cfg.act)
+    default_threads = cref.threads()
+    cref.set_threads(threads or default_threads)
+    used_threads = cref.threads()
+    E, d, d_ff = cfg.E, cfg.d, cfg.d_ff
+    wr = _host_decode(inp["W_r"], cfg.act, torch)
     rb = None if inp["router_bias"] is None else inp["router_bias"].cpu().numpy()
     sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
-    xall = host(inp["x"], cfg.act)
+    b1, b2 = _host_decode(inp["b1"], cfg.act, torch), _host_decode(inp["b2"], cfg.act, torch)
+    W1 = np.zeros((E, d_ff, d))      # zero pages until an expert is filled in
+    W2 = np.zeros((E, d, d_ff))
+    have = set()
 
-    def run(n):
+    def sample(n):
+        x = _host_decode(inp["x"][:n], cfg.act, torch)
+        idx, _ = cref.route(cref.router_logits(x, wr, rb), cfg.K, sb, cfg.n_groups, cfg.topk_groups,
+                            cfg.renormalize)
+        used = sorted(set(int(e) for e in np.unique(idx)))
+        for e in used:
+            if e not in have:
+                W1[e] = _host_decode(inp["W1"][e], cfg.w, torch, inp["w1_scale"][e] if cfg.w == "fp8" else None)
+                W2[e] = _host_decode(inp["W2"][e], cfg.w, torch, inp["w2_scale"][e] if cfg.w == "fp8" else None)
+                have.add(e)
+        return x, len(used)
+
+    def run(x):
         t0 = time.perf_counter()
-        cref.layer_forward(xall[:n], wr, W1, b1, W2, b2, K=cfg.K, router_bias=rb, select_bias=sb,
-                           n_groups=cfg.n_groups, topk_groups=cfg.topk_groups, renormalize=cfg.renormalize)
+        cref.layer_forward(x, wr, W1, b1, W2, b2, K=cfg.K, router_bias=rb, select_bias=sb, n_groups=cfg.n_groups,
+                           topk_groups=cfg.topk_groups, renormalize=cfg.renormalize)
         return time.perf_counter() - t0
 
-    n = min(cfg.S, 16)
-    t = run(n)
-    while t < 0.5 * target_s and n < cfg.S:
-        n = int(min(cfg.S, n * min(8.0, max(2.0, target_s / max(t, 1e-3)))))
-        t = run(n)
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {cfg.S} tokens of {cfg.name}: plain C++ loops (double, OpenMP), "
-                      f"weights decoded beforehand; {t:.1f}s", "seconds": round(t, 2)}
+    try:
+        if n_tokens is not None:
+            n = min(cfg.S, n_tokens)
+            x, ne = sample(n)
+            ts = [run(x) for _ in range(repeats)]
+            t = statistics.median(ts)
+        else:
+            n = min(cfg.S, 4)
+            x, ne = sample(n)
+            t = run(x)
+            while t < 0.5 * budget_s and n < cfg.S:
+                grow = 2.0 if max_experts is not None else min(8.0, max(2.0, budget_s / max(t, 1e-3)))
+                n2 = int(min(cfg.S, n * grow))
+                x2, ne2 = sample(n2)
+                if max_experts is not None and ne2 > max_experts:
+                    break
+                n, x, ne = n2, x2, ne2
+                t = run(x)
+            ts = [t]
+    finally:
+        cref.set_threads(default_threads)
+    return {"value": round(n / t, 3), "unit": "tokens/s", "tokens": n, "of": cfg.S, "experts_touched": ne,
+            "seconds": round(t, 3), "runs": len(ts), "threads": used_threads}
 
 
-def cpu_baseline(cfg, w, target_s, torch):
-    """The oracle, as it is, on the first n tokens of the same workload."""
+def cpu_numpy_rate(cfg, w, target_s, torch):
+    """The numpy oracle (oracle/moe_oracle.py, float64, BLAS products) as it
+    stands on the first n tokens of the same workload."""
     import numpy as np
 
     import oracle as O
@@ -588,17 +721,23 @@ def cpu_baseline(cfg, w, target_s, torch):
                         w1_scale=host["w1_scale"], w2_scale=host["w2_scale"])
         return time.perf_counter() - t0
 
-    # grow the sample until it costs about target_s of CPU time (or covers S)
     n = min(cfg.S, 32)
     t = run(n)
     while t < 0.5 * target_s and n < cfg.S:
         n = int(min(cfg.S, n * min(8.0, max(2.0, target_s / max(t, 1e-3)))))
         t = run(n)
     threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas") or 1
-    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {cfg.S} tokens of {cfg.name}: routing, every expert they touch "
-                      f"(float64, weights decoded per expert), combine; {t:.1f}s",
+    return {"value": round(n / t, 2), "unit": "tokens/s", "blas_threads": threads, "tokens": n, "of": cfg.S,
             "seconds": round(t, 2)}
+
+
+def host_cores():
+    """Logical CPUs this process may run on, and the machine's count."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count()
+    return aff, os.cpu_count()
 
 
 def main():
@@ -625,21 +764,31 @@ def main():
     if a.pmc_probe:
         pmc_probe(a, D, M, torch)
         return
-    cfg, w, ms, stage_ms, touched, counts = run_workload(a.workload, a.steps, a.warmup, D, M, torch)
+    cpu = not a.no_cpu_baseline
+    cpu_legs = {}
+    cfg, w, (ms, med), st, touched, counts = run_workload(a.workload, a.steps, a.warmup, D, M, torch)
+    stage_ms, stage_med = stage_dicts(st)
     mean = cfg.S * cfg.K / cfg.E
     out = {
-        "metric": METRIC, "value": round(cfg.S / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "metric": METRIC, "value": round(cfg.S / (med / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(med, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.act, "data": "synthetic",
         "config": {"workload": cfg.name, "S": cfg.S, "d": cfg.d, "d_ff": cfg.d_ff, "E": cfg.E, "K": cfg.K,
                    "weights": cfg.w, "max_over_mean_load": round(float(counts.max()) / mean, 3),
                    "experts_touched": touched},
+        "statistic": "median of per-step HIP-event times (value, ms_per_step); mean in ms_per_step_mean",
+        "ms_per_step_mean": round(ms, 4),
         "roofline": roofline(cfg, stage_ms, touched, cfg.name),
-        "layer": layer_fractions(cfg, ms, touched, "bf16" if cfg.act == "bf16" else "f32"),
-        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "layer_tflops": round(4.0 * cfg.S * cfg.K * cfg.d * cfg.d_ff / (ms / 1e3) / 1e12, 2),
+        "layer": layer_fractions(cfg, med, touched, "bf16" if cfg.act == "bf16" else "f32"),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}, "stage_ms_median": stage_med,
+        "layer_tflops": round(4.0 * cfg.S * cfg.K * cfg.d * cfg.d_ff / (med / 1e3) / 1e12, 2),
     }
-    log(f"[bench] {cfg.name}: {ms:.3f} ms/step, stages {out['stage_ms']}")
+    log(f"[bench] {cfg.name}: {med:.3f} ms/step (mean {ms:.3f}), stages {out['stage_ms']}")
+    if cpu:
+        cpu_legs[cfg.name] = cpu_loops_rate(cfg, w.inp, a.cpu_seconds / 2, torch)
+        log(f"[bench] cpu loops {cfg.name}: {cpu_legs[cfg.name]}")
+        one = cpu_loops_rate(cfg, w.inp, 0, torch, threads=1, n_tokens=4)
+        log(f"[bench] cpu loops {cfg.name}, one thread: {one}")
     if not a.no_context and cfg.act == "bf16":
         out["context"] = context_leg(w, torch, counts.tolist())
         out["context"]["this_up_TFLOPs"] = out["roofline"]["achieved"] if out["roofline"]["kernel"] == "expert_up" \
@@ -648,37 +797,70 @@ def main():
     if not a.no_capacity:
         out["capacity"] = capacity_leg(w, M, torch, 1.25, a.steps)
         log(f"[bench] capacity: {out['capacity']}")
+    if cpu:
+        out["cpu_numpy"] = cpu_numpy_rate(cfg, w, a.cpu_seconds / 2, torch)
+    del w
+    torch.cuda.empty_cache()
     if not a.no_w8a8:
-        out["w8a8"] = w8a8_leg(D, M, torch, max(5, a.steps // 2), 3)
+        out["w8a8"] = w8a8_leg(D, M, torch, max(5, a.steps // 2), 3, a.cpu_seconds / 3 if cpu else 0.0)
+        if cpu and out["w8a8"].get("cpu_loops"):
+            cpu_legs["dsv3_fp8"] = out["w8a8"].pop("cpu_loops")
         log(f"[bench] w8a8: {out['w8a8']}")
     if not a.no_decode and cfg.name != "decode":
-        dcfg, dw, dms, dstage, dtouched, _ = run_workload("decode", max(a.steps, 100), a.warmup, D, M, torch)
-        out["decode"] = {"workload": "decode", "tokens_per_s": round(dcfg.S / (dms / 1e3), 1),
-                         "ms_per_step": round(dms, 4), "roofline": roofline(dcfg, dstage, dtouched, "decode"),
-                         "layer": layer_fractions(dcfg, dms, dtouched, "bf16"),
-                         "stage_ms": {k: round(v, 4) for k, v in dstage.items()},
+        dcfg, dw, (dms, dmed), dst, dtouched, _ = run_workload("decode", max(a.steps, 100), a.warmup, D, M, torch)
+        dmean, dmedian = stage_dicts(dst)
+        out["decode"] = {"workload": "decode", "tokens_per_s": round(dcfg.S / (dmed / 1e3), 1),
+                         "ms_per_step": round(dmed, 4), "ms_per_step_mean": round(dms, 4),
+                         "experts_touched": dtouched,
+                         "roofline": roofline(dcfg, dmean, dtouched, "decode"),
+                         "layer": layer_fractions(dcfg, dmed, dtouched, "bf16"),
+                         "stage_ms": {k: round(v, 4) for k, v in dmean.items()}, "stage_ms_median": dmedian,
                          "graph": graph_leg(dw, torch, max(a.steps, 100), a.warmup)}
+        if cpu:
+            cpu_legs["decode"] = cpu_loops_rate(dcfg, dw.inp, 0, torch, n_tokens=dcfg.S)
         del dw
+        torch.cuda.empty_cache()
     if not a.no_skew and cfg.name != "zipf_skew":
-        zcfg, zw, zms, zstage, ztouched, zcounts = run_workload("zipf_skew", a.steps, a.warmup, D, M, torch)
-        gemm_ms = zstage["expert_up"] + zstage["expert_down"]
+        zcfg, zw, (zms, zmed), zst, ztouched, zcounts = run_workload("zipf_skew", a.steps, a.warmup, D, M, torch)
+        zmean, zmedian = stage_dicts(zst)
+        gemm_ms = zmean["expert_up"] + zmean["expert_down"]
         ffn_flops = 4.0 * zcfg.S * zcfg.K * zcfg.d * zcfg.d_ff
-        out["zipf_skew"] = {"workload": "zipf_skew", "tokens_per_s": round(zcfg.S / (zms / 1e3), 1),
-                            "ms_per_step": round(zms, 4),
+        out["zipf_skew"] = {"workload": "zipf_skew", "tokens_per_s": round(zcfg.S / (zmed / 1e3), 1),
+                            "ms_per_step": round(zmed, 4), "ms_per_step_mean": round(zms, 4),
                             "max_over_mean_load": round(float(zcounts.max()) / (zcfg.S * zcfg.K / zcfg.E), 3),
                             "empty_experts": zcfg.E - ztouched,
-                            "roofline": roofline(zcfg, zstage, ztouched, "zipf_skew"),
+                            "roofline": roofline(zcfg, zmean, ztouched, "zipf_skew"),
                             "gemms_mfma_frac": round(ffn_flops / (gemm_ms / 1e3) / (PEAK_TFLOPS["bf16"] * 1e12), 4),
-                            "layer": layer_fractions(zcfg, zms, ztouched, "bf16"),
-                            "stage_ms": {k: round(v, 4) for k, v in zstage.items()}}
-        log(f"[bench] zipf_skew: {zms:.3f} ms/step, stages {out['zipf_skew']['stage_ms']}")
+                            "layer": layer_fractions(zcfg, zmed, ztouched, "bf16"),
+                            "stage_ms": {k: round(v, 4) for k, v in zmean.items()}, "stage_ms_median": zmedian}
+        log(f"[bench] zipf_skew: {zmed:.3f} ms/step, stages {out['zipf_skew']['stage_ms']}")
+        if cpu:
+            cpu_legs["zipf_skew"] = cpu_loops_rate(zcfg, zw.inp, a.cpu_seconds / 3, torch)
         del zw
         torch.cuda.empty_cache()
-    if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, w, a.cpu_seconds, torch)
-        loops = cpu_loops_baseline(cfg, w, a.cpu_seconds / 2, torch)
-        if loops is not None:
-            out["cpu_baseline"]["cpp_loops"] = loops
+    if cpu:
+        tcfg = D.CONFIGS["tiny_f32"]
+        tinp = D.make_inputs(tcfg, "cpu")
+        cpu_legs["tiny_f32"] = cpu_loops_rate(tcfg, tinp, 0, torch, n_tokens=tcfg.S, repeats=10)
+        tiny_one = cpu_loops_rate(tcfg, tinp, 0, torch, threads=1, n_tokens=tcfg.S, repeats=3)
+        aff, ncpu = host_cores()
+        gpu_rates = {cfg.name: out["value"], "decode": out.get("decode", {}).get("tokens_per_s"),
+                     "zipf_skew": out.get("zipf_skew", {}).get("tokens_per_s"),
+                     "dsv3_fp8": out.get("w8a8", {}).get("tokens_per_s_w8a16")}
+        for k, v in cpu_legs.items():
+            if v is not None and gpu_rates.get(k):
+                v["gpu_tokens_per_s"] = gpu_rates[k]
+        main_leg = cpu_legs[cfg.name]
+        out["cpu_baseline"] = {
+            "value": main_leg["value"], "unit": "tokens/s", "cores": main_leg["threads"], "kind": "oracle",
+            "sample": f"first {main_leg['tokens']} of {cfg.S} tokens of {cfg.name}: the plain C++ loops of the "
+                      f"oracle (double, OpenMP over tokens, {main_leg['threads']} threads), one call, "
+                      f"{main_leg['seconds']}s; weights decoded beforehand",
+            "host_cpus_available": aff, "host_cpus_total": ncpu,
+            "single_thread": {"tiny_f32_64_tokens": tiny_one, cfg.name: one},
+            "per_config": cpu_legs,
+            "numpy_oracle": out.pop("cpu_numpy", None),
+        }
     print(json.dumps(out), flush=True)
 
 

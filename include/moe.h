@@ -209,6 +209,29 @@ int32_t moe_expert_down(const moe_problem* p, const void* h, const int32_t* expe
                         const float* w2_scale, void* y_perm, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* The two expert products with fp8 activations (W8A8, "MoE 推理工程深层实战"
+ * section 3.3: FP8 E4M3 experts), stage by stage, for a problem with
+ * act_quant = 1 (else MOE_ERR_INVALID_ARG):
+ *   moe_expert_up_a8:   h[r]      = GeLU(dq(x8[r]) W1_e + b1_e)        (bf16)
+ *   moe_expert_down_a8: y_perm[r] = dq(h8[r]) W2_e + b2_e             (bf16)
+ * where dq(codes[r]) = decode(codes[r]) * scale[r]: e4m3 rows with one
+ * float32 scale per row, as moe_quantize_rows writes them (the layer with
+ * act_quant = 1 runs exactly moe_permute's gather, moe_quantize_rows of the
+ * gathered rows, moe_expert_up_a8, moe_quantize_rows of h,
+ * moe_expert_down_a8).  Both operands go to the fp8 MFMAs; the float32 sum
+ * is multiplied by row scale x channel scale in the epilogue.
+ *   x8 [rows_capacity][d], h8 [rows_capacity][d_ff]: uint8 codes;
+ *   x_scale, h_scale [rows_capacity] float32; w1_scale / w2_scale required.
+ *   Other arguments and ws as for moe_expert_up / moe_expert_down. */
+int32_t moe_expert_up_a8(const moe_problem* p, const uint8_t* x8, const float* x_scale,
+                         const int32_t* expert_counts, const int32_t* expert_offsets,
+                         const void* W1, const void* b1, const float* w1_scale, void* h,
+                         void* ws, size_t ws_bytes, void* stream);
+int32_t moe_expert_down_a8(const moe_problem* p, const uint8_t* h8, const float* h_scale,
+                           const int32_t* expert_counts, const int32_t* expert_offsets,
+                           const void* W2, const void* b2, const float* w2_scale, void* y_perm,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* Combine (chapter 11 sections 11.1.1 and 11.2.1; "MoE 混合专家推理", one
  * MoE forward): y[t] = sum over k = 0..K-1, in slot order, of
  * topk_gate[t][k] * y_perm[inv_perm[t*K+k]], accumulated in float32 and

@@ -54,8 +54,20 @@ def lib() -> ctypes.CDLL:
                                            _c32, _c32, _c32, _c32, _c32, _c32, ctypes.c_double,
                                            _Opt(np.float32), _d, _i32, _d]
         L.oracle_layer_forward.restype = _c32
+        L.oracle_set_threads.argtypes = [_c32]
+        L.oracle_threads.restype = _c32
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Threads of the OpenMP loops (the library's default: OMP_NUM_THREADS or
+    every hardware thread)."""
+    lib().oracle_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())
 
 
 def decode(arr: np.ndarray, dtype: str) -> np.ndarray:

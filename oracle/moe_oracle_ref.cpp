@@ -21,6 +21,8 @@
 // renormalised over the K chosen (renormalize = 1) or as full-softmax
 // probabilities (renormalize = 0); GeLU is x * Phi(x) with erf; the experts'
 // rows keep token order.
+#include <omp.h>
+
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -51,6 +53,10 @@ double gelu(double a) { return 0.5 * a * (1.0 + std::erf(a / std::sqrt(2.0))); }
 }  // namespace
 
 extern "C" {
+
+// Threads the loops below use (OpenMP): set, and query.
+void oracle_set_threads(int32_t n) { omp_set_num_threads(n > 0 ? n : 1); }
+int32_t oracle_threads(void) { return omp_get_max_threads(); }
 
 void oracle_decode_bf16(const uint16_t* src, int64_t n, double* dst) {
   for (int64_t i = 0; i < n; ++i) dst[i] = bf16_value(src[i]);

@@ -20,6 +20,7 @@ __all__ = [
     "moe_workspace_bytes", "moe_tile_m", "moe_rows_capacity", "moe_status_string",
     "workspace", "moe_load_stats", "moe_apply_capacity", "moe_quantize_rows", "STAGE_CAPACITY", "MOE_STATS_N", "STAT_NAMES", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
     "moe_layer_forward_noalloc", "MOE_ERR_TOO_LARGE", "MOE_NOALLOC_SCRATCH_BYTES",
+    "moe_expert_up_a8", "moe_expert_down_a8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfl_moe.so")
@@ -73,6 +74,8 @@ _SIGS = {
     "moe_expert_ffn": (_i32, [_P] + [_vp] * 11 + [_vp, _sz, _vp]),
     "moe_expert_up": (_i32, [_P] + [_vp] * 7 + [_vp, _sz, _vp]),
     "moe_expert_down": (_i32, [_P] + [_vp] * 7 + [_vp, _sz, _vp]),
+    "moe_expert_up_a8": (_i32, [_P] + [_vp] * 8 + [_vp, _sz, _vp]),
+    "moe_expert_down_a8": (_i32, [_P] + [_vp] * 8 + [_vp, _sz, _vp]),
     "moe_combine": (_i32, [_P] + [_vp] * 4 + [_vp]),
     "moe_layer_forward": (_i32, [_P] + [_vp] * 15 + [_vp, _sz, _vp]),
     "moe_layer_forward_noalloc": (_i32, [_P] + [_vp] * 15 + [_vp]),
@@ -250,6 +253,36 @@ def moe_expert_down(p, h, expert_counts, expert_offsets, W2, b2, w2_scale=None, 
                                _ptr(W2), _ptr(b2), _ptr(w2_scale), _ptr(y_perm), _ptr(ws), ws.numel(),
                                _stream(stream))
     _check("moe_expert_down", st)
+    return y_perm
+
+
+def moe_expert_up_a8(p, x8, x_scale, expert_counts, expert_offsets, W1, b1, w1_scale, h=None, ws=None,
+                     stream=None):
+    """W8A8 up product (p.act_quant = 1): e4m3 rows x8 with row scales -> bf16 h."""
+    side = _side(stream)
+    if h is None:
+        h = _empty((moe_rows_capacity(p), p.d_ff), torch.bfloat16, x8.device, side)
+    if ws is None:
+        ws = workspace(p, STAGE_EXPERT_FFN, x8.device, side)
+    st = lib().moe_expert_up_a8(ctypes.byref(p), _ptr(x8), _ptr(x_scale), _ptr(expert_counts),
+                                _ptr(expert_offsets), _ptr(W1), _ptr(b1), _ptr(w1_scale), _ptr(h), _ptr(ws),
+                                ws.numel(), _stream(stream))
+    _check("moe_expert_up_a8", st)
+    return h
+
+
+def moe_expert_down_a8(p, h8, h_scale, expert_counts, expert_offsets, W2, b2, w2_scale, y_perm=None, ws=None,
+                       stream=None):
+    """W8A8 down product (p.act_quant = 1): e4m3 rows h8 with row scales -> bf16 y_perm."""
+    side = _side(stream)
+    if y_perm is None:
+        y_perm = _empty((moe_rows_capacity(p), p.d), torch.bfloat16, h8.device, side)
+    if ws is None:
+        ws = workspace(p, STAGE_EXPERT_FFN, h8.device, side)
+    st = lib().moe_expert_down_a8(ctypes.byref(p), _ptr(h8), _ptr(h_scale), _ptr(expert_counts),
+                                  _ptr(expert_offsets), _ptr(W2), _ptr(b2), _ptr(w2_scale), _ptr(y_perm),
+                                  _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_expert_down_a8", st)
     return y_perm
 
 

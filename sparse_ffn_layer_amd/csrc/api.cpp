@@ -391,6 +391,43 @@ int32_t moe_expert_down(const moe_problem* mp, const void* h, const int32_t* exp
                                        (hipStream_t)stream, nullptr));
 }
 
+// W8A8 stage entry points: e4m3 rows with per-row scales in, bf16 out.
+int32_t check_expert_a8(const moe_problem* mp, Problem* p, std::initializer_list<const void*> req) {
+  int32_t s = check_problem(mp, p);
+  if (s != MOE_OK) return s;
+  if (!p->act_quant) return MOE_ERR_INVALID_ARG;
+  if (p->S == 0) return MOE_OK;
+  for (const void* q : req)
+    if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int32_t moe_expert_up_a8(const moe_problem* mp, const uint8_t* x8, const float* x_scale,
+                         const int32_t* expert_counts, const int32_t* expert_offsets, const void* W1,
+                         const void* b1, const float* w1_scale, void* h, void* ws, size_t ws_bytes,
+                         void* stream) {
+  Problem p;
+  int32_t s = check_expert_a8(mp, &p, {x8, x_scale, expert_counts, expert_offsets, W1, b1, w1_scale, h});
+  if (s != MOE_OK || p.S == 0) return s;
+  size_t usable = 0;
+  float* split = split_region(ws, ws_bytes, &usable);
+  return hip_status(launch_expert_up(p, rows_capacity(p), x8, expert_counts, expert_offsets, W1, b1, w1_scale,
+                                     h, split, usable, (hipStream_t)stream, x_scale));
+}
+
+int32_t moe_expert_down_a8(const moe_problem* mp, const uint8_t* h8, const float* h_scale,
+                           const int32_t* expert_counts, const int32_t* expert_offsets, const void* W2,
+                           const void* b2, const float* w2_scale, void* y_perm, void* ws, size_t ws_bytes,
+                           void* stream) {
+  Problem p;
+  int32_t s = check_expert_a8(mp, &p, {h8, h_scale, expert_counts, expert_offsets, W2, b2, w2_scale, y_perm});
+  if (s != MOE_OK || p.S == 0) return s;
+  size_t usable = 0;
+  float* split = split_region(ws, ws_bytes, &usable);
+  return hip_status(launch_expert_down(p, rows_capacity(p), h8, expert_counts, expert_offsets, W2, b2,
+                                       w2_scale, y_perm, split, usable, (hipStream_t)stream, h_scale));
+}
+
 int32_t moe_combine(const moe_problem* mp, const void* y_perm, const int32_t* inv_perm,
                     const float* topk_gate, void* y, void* stream) {
   Problem p;

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -267,6 +267,16 @@ def test_fp8_activation_checks():
     assert lib.moe_expert_ffn(ctypes.byref(p), *([a] * 11), a, 1 << 30, None) == M.MOE_ERR_UNSUPPORTED
     assert lib.moe_expert_up(ctypes.byref(p), *([a] * 7), None, 0, None) == M.MOE_ERR_UNSUPPORTED
     assert lib.moe_expert_down(ctypes.byref(p), *([a] * 7), None, 0, None) == M.MOE_ERR_UNSUPPORTED
+    # the W8A8 stage products: they need act_quant = 1 and every pointer
+    assert lib.moe_expert_up_a8(ctypes.byref(prob(w="fp8")), *([a] * 8), None, 0, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down_a8(ctypes.byref(prob(w="fp8")), *([a] * 8), None, 0, None) == M.MOE_ERR_INVALID_ARG
+    for i in range(8):
+        args = [a] * 8
+        args[i] = None
+        assert lib.moe_expert_up_a8(ctypes.byref(p), *args, None, 0, None) == M.MOE_ERR_INVALID_ARG
+        args[i] = odd
+        assert lib.moe_expert_down_a8(ctypes.byref(p), *args, None, 0, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_up_a8(ctypes.byref(prob(w="fp8", act_quant=1, S=0)), *([None] * 8), None, 0, None) == 0
     # the row quantiser
     q = lib.moe_quantize_rows
     assert q(a, -1, 64, a, a, None) == M.MOE_ERR_INVALID_ARG

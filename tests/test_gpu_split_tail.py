@@ -47,7 +47,7 @@ def _split_vs_plain(a, b, rows):
     return err / scale
 
 
-def _oracle_rows(cfg, ov, pm, idx, experts, h, y_perm):
+def _oracle_rows(cfg, ov, pm, idx, experts, h, y_perm, ffn=O.expert_ffn):
     """Every routed row of `experts`: h and y_perm against the oracle's expert
     FFN (y_perm computed by the GPU from its own h)."""
     flat_e = idx.reshape(-1)
@@ -61,8 +61,8 @@ def _oracle_rows(cfg, ov, pm, idx, experts, h, y_perm):
         x64 = O.decode(ov["x"][flat_t[ps]], cfg.act)
         W1e = O.expert_matrix(ov["W1"][e], cfg.w, None if ov["w1_scale"] is None else ov["w1_scale"][e])
         W2e = O.expert_matrix(ov["W2"][e], cfg.w, None if ov["w2_scale"] is None else ov["w2_scale"][e])
-        hr, yr = O.expert_ffn(x64, W1e, O.decode(ov["b1"][e], cfg.act), W2e, O.decode(ov["b2"][e], cfg.act),
-                              return_hidden=True)
+        hr, yr = ffn(x64, W1e, O.decode(ov["b1"][e], cfg.act), W2e, O.decode(ov["b2"][e], cfg.act),
+                     return_hidden=True)
         rows = torch.from_numpy(pm["inv_perm"][ps].astype(np.int64)).to(DEV)
         hg = O.decode(raw(h[rows]), cfg.act)
         yg = O.decode(raw(y_perm[rows]), cfg.act)
@@ -209,3 +209,49 @@ def test_w8a8_dsv3_split_tail_tokens():
     tokens = np.unique(np.concatenate([picked, rest, [cfg.S - 1]]))
     print(f"w8a8 dsv3: split tiles {len(tails)} owned by {len(owners)} experts; {tokens.size} tokens", flush=True)
     _w8a8_check(cfg, inp, tokens, y, idx, gate, lg)
+
+
+def test_dsv3_w8a8_products_split_tail_experts_every_row():
+    """The W8A8 stage entry points at the DeepSeek shape: x_perm quantised
+    per row, the up product with the split tail against the unsplit launch on
+    every valid row, h quantised per row, the same for the down product; and
+    every row of each expert owning a split tile (BK = 128) plus 16 spread
+    experts against the oracle's W8A8 expert FFN."""
+    cfg = D.CONFIGS["dsv3_fp8"]
+    inp = gpu_inputs("dsv3_fp8")
+    ov = oracle_view(inp)
+    p = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                       cfg.renormalize, 1.0, 0, 1)
+    assert M.moe_tile_m(p) == BM
+    idx, _ = oracle_select(cfg, oracle_logits(cfg, ov), ov)
+    pm = O.permute(idx, cfg.E, BM)
+    cap = M.moe_rows_capacity(p)
+    x_perm = act_from_raw(host_x_perm(cfg, ov["x"], pm, cap), cfg.act)
+    counts = torch.from_numpy(pm["counts"]).to(DEV)
+    offsets = torch.from_numpy(pm["offsets"]).to(DEV)
+    none = torch.empty(1, dtype=torch.uint8, device=DEV)
+    print("dsv3 W8A8 products, split vs unsplit", flush=True)
+    x8, xs = M.moe_quantize_rows(x_perm)
+    hz = lambda: torch.zeros((cap, cfg.d_ff), dtype=torch.bfloat16, device=DEV)   # padding rows stay 0
+    up = lambda ws=None: M.moe_expert_up_a8(p, x8, xs, counts, offsets, inp["W1"], inp["b1"], inp["w1_scale"],
+                                            h=hz(), ws=ws)
+    h, h2, h0 = up(), up(), up(none)
+    h8, hs = M.moe_quantize_rows(h)
+    down = lambda ws=None: M.moe_expert_down_a8(p, h8, hs, counts, offsets, inp["W2"], inp["b2"],
+                                                inp["w2_scale"], ws=ws)
+    y, y2, y0 = down(), down(), down(none)
+    sync()
+    rows = valid_rows(pm["counts"], pm["offsets"])
+    vi = torch.from_numpy(rows).to(DEV)
+    assert torch.equal(h[vi], h2[vi]) and torch.equal(y[vi], y2[vi])
+    _split_vs_plain(h, h0, rows)
+    _split_vs_plain(y, y0, rows)
+    up_tails = split_tail_tiles(pm["offsets"], cap, cfg.d_ff, cfg.d, BM, BN, 128, GM)
+    down_tails = split_tail_tiles(pm["offsets"], cap, cfg.d, cfg.d_ff, BM, BN, 128, GM)
+    assert up_tails
+    owners = sorted(set(e for _, _, e in up_tails + down_tails))
+    spread = [int(e) for e in np.linspace(0, cfg.E - 1, 16).round()]
+    print(f"split tiles {len(up_tails)} + {len(down_tails)}, owned by experts {owners}", flush=True)
+    n = _oracle_rows(cfg, ov, pm, idx, owners + spread, h, y, ffn=O.expert_ffn_w8a8)
+    print(f"compared {n} routed rows of {len(set(owners + spread))} experts", flush=True)
+    assert n >= 20 * 64
