@@ -140,11 +140,42 @@ __device__ __forceinline__ int swz(int r) {
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
-// Tile L of the persistent order: bands of GM row tiles, the row tile varying
+// Tile L of the persistent order: bands of row tiles, the row tile varying
 // fastest inside a band.  False if the tile has no valid rows.
+//  GM > 0: bands of GM consecutive row tiles of the whole tile space.
+//  GM < 0: expert-aligned bands: each group's row tiles split into bands of
+//  at most -GM row tiles starting at its first row tile, so the row tiles of
+//  one expert run side by side on one XCD and read each slice of a weight
+//  panel from HBM once, the others finding it in that XCD's L2.  The bands
+//  sit in the tile space exactly where their row tiles are (row tile r
+//  covers positions [r n_tiles, (r + 1) n_tiles)), so tile L finds its band
+//  with the same binary search over the offsets that finds its expert.
 template <int BM, int BN, int GM>
 __device__ __forceinline__ bool tile_coords(const GemmArgs& a, int m_used, int64_t L, int64_t& row0, int& n0,
                                             int& g, int& rows) {
+  if constexpr (GM < 0) {
+    if (a.offsets == nullptr) return tile_coords<BM, BN, 1>(a, m_used, L, row0, n0, g, rows);
+    constexpr int GB = -GM;
+    const int r = (int)(L / a.n_tiles);
+    const int64_t rr = (int64_t)r * BM;
+    if (rr >= a.offsets[a.G]) return false;
+    int lo = 0, hi = a.G;  // offsets[lo] <= rr < offsets[lo + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.offsets[mid] <= rr) lo = mid; else hi = mid;
+    }
+    const int first = a.offsets[lo] / BM, rt = (a.offsets[lo + 1] - a.offsets[lo]) / BM;
+    const int bi = (r - first) / GB;
+    const int bfirst = first + bi * GB;
+    const int gm = rt - bi * GB < GB ? rt - bi * GB : GB;
+    const int64_t local = L - (int64_t)bfirst * a.n_tiles;
+    row0 = (int64_t)(bfirst + (int)(local % gm)) * BM;
+    n0 = (int)(local / gm) * BN;
+    g = lo;
+    const int64_t left = a.counts[g] - (row0 - a.offsets[g]);
+    rows = (int)(left < BM ? left : BM);
+    return rows > 0;
+  }
   const int64_t band = (int64_t)GM * a.n_tiles;
   const int64_t bnd = L / band;
   const int first_m = (int)(bnd * GM);
@@ -766,11 +797,11 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& a, const f32x16_t (&
 // tile's first stage the same way, so those loads fly during the epilogue.
 // Rows of a partly filled tile do all MFMAs (their loads read zeros); only
 // the stores skip them.
-// Row tiles per band of the four-wave kernel's tile order.  The up product
-// (many channel tiles) gains from taller bands: each band re-reads the
-// weights of its experts once, and 8 row tiles halve those passes (measured
-// 1-2 % on expert_up at the Mixtral and Zipf shapes; no gain on down).
-constexpr int w4_band(int epi) { return epi == EPI_GELU ? 8 : 4; }
+// Bands of the four-wave kernel's tile order: expert-aligned, up to 8 row
+// tiles (each band re-reads the weights of its expert once; against bands
+// of 8 (up) and 4 (down) consecutive row tiles of the whole tile space:
+// Mixtral shape 1.96 -> 1.94 ms/step, Zipf shape 1.86 -> 1.82 ms/step).
+constexpr int w4_band(int) { return -8; }
 
 template <int EPI>
 __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const GemmArgs a) {
@@ -1224,15 +1255,22 @@ static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hi
   switch (regime) {
     case 0:
       if (!BFP8 && n256 && a.K % 64 == 0) return run_bf16_w4<EPI>(a, rows_cap, st, pb);
-      if (n256) return run_bf16<256, 256, 64, 4, 2, 2, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
-      if (n128) return run_bf16<256, 128, 64, 4, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
-      return run_bf16<256, 64, 64, 4, 1, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
+      if (n256) return run_bf16<256, 256, 64, 4, 2, 2, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);
+      if (n128) return run_bf16<256, 128, 64, 4, 2, 3, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);
+      return run_bf16<256, 64, 64, 4, 1, 3, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);
     case 1:
-      // bands of 2 row tiles: 1-2 % faster than 4 or 8 on the fp8-weight
-      // DeepSeek shape (both activation types), whose weights stream from HBM
-      if (n256) return run_bf16<128, 256, 64, 2, 4, 3, BFP8, EPI, 2, 32>(a, rows_cap, st, pb);
-      if (n128) return run_bf16<128, 128, 64, 2, 4, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
-      return run_bf16<128, 64, 64, 2, 2, 3, BFP8, EPI, 4, 32>(a, rows_cap, st, pb);
+      // expert-aligned bands of up to 4 row tiles: the row tiles of an expert
+      // share each weight panel through L2 (fp8-weight DeepSeek shape, W8A8:
+      // 2.53 -> 2.39 ms/step against bands of 2 consecutive row tiles)
+      if constexpr (BFP8) {
+        // fp8 weights: k stages of 128, so each stage reads whole 128-byte
+        // lines of every weight row (W8A16 DeepSeek shape 3.47 -> 3.31
+        // ms/step against stages of 64 with three slots)
+        if (n256 && k128) return run_bf16<128, 256, 128, 2, 4, 2, true, EPI, -4, 32>(a, rows_cap, st, pb);
+      }
+      if (n256) return run_bf16<128, 256, 64, 2, 4, 3, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);
+      if (n128) return run_bf16<128, 128, 64, 2, 4, 3, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);
+      return run_bf16<128, 64, 64, 2, 2, 3, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);
     default:
       if (k128) return run_bf16<16, 64, 128, 1, 4, 3, BFP8, EPI, 1>(a, rows_cap, st, pb);
       return run_bf16<16, 64, 64, 1, 2, 8, BFP8, EPI, 1>(a, rows_cap, st, pb);  // 128 threads: A tile is 128 chunks
@@ -1245,9 +1283,9 @@ template <int EPI>
 static hipError_t run_regime_a8(int regime, const GemmArgs& a, int64_t rows_cap, hipStream_t st, size_t pb) {
   const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0, k256 = a.K % 256 == 0;
   if (regime <= 1) {
-    if (n256) return run_bf16<128, 256, 128, 2, 4, 3, true, EPI, 2, 32, true>(a, rows_cap, st, pb);
-    if (n128) return run_bf16<128, 128, 128, 2, 4, 3, true, EPI, 4, 32, true>(a, rows_cap, st, pb);
-    return run_bf16<128, 64, 128, 2, 2, 3, true, EPI, 4, 32, true>(a, rows_cap, st, pb);
+    if (n256) return run_bf16<128, 256, 128, 2, 4, 3, true, EPI, -4, 32, true>(a, rows_cap, st, pb);
+    if (n128) return run_bf16<128, 128, 128, 2, 4, 3, true, EPI, -4, 32, true>(a, rows_cap, st, pb);
+    return run_bf16<128, 64, 128, 2, 2, 3, true, EPI, -4, 32, true>(a, rows_cap, st, pb);
   }
   if (k256) return run_bf16<16, 64, 256, 1, 4, 5, true, EPI, 1, 16, true>(a, rows_cap, st, pb);
   return run_bf16<16, 64, 128, 1, 2, 8, true, EPI, 1, 16, true>(a, rows_cap, st, pb);

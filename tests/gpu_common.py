@@ -93,8 +93,10 @@ def near_tie(keys_row, K, gap):
 def split_tail_tiles(offsets, rows_cap, N, K, BM, BN, BK, GM, grid=256):
     """Tiles whose k range the grouped GEMM splits: the host-side replica of
     its persistent schedule.  The tile space (row tiles in use x N / BN
-    channel tiles, in bands of GM row tiles, the row tile fastest) is cut into
-    8 contiguous slices, one per XCD; each slice runs in rounds of its
+    channel tiles, in bands of row tiles, the row tile fastest: GM > 0 bands
+    of GM consecutive row tiles, GM < 0 bands of at most -GM row tiles
+    starting at each expert's first row tile) is cut into 8 contiguous
+    slices, one per XCD; each slice runs in rounds of its
     grid / 8 workgroups, and when its last round is partial with at least
     twice as many idle workgroups as tail tiles and K / BK >= 16 k-tiles,
     the tail tiles run split along k.  `grid` is the launch's workgroup
@@ -122,12 +124,22 @@ def split_tail_tiles(offsets, rows_cap, N, K, BM, BN, BK, GM, grid=256):
             continue
         for tau in range(tail):
             L = full_end + tau
-            band = GM * n_tiles
-            bnd = L // band
-            first_m = bnd * GM
-            gm = min(m_used - first_m, GM)
-            rem = L - bnd * band
-            mt, nt = first_m + rem % gm, rem // gm
+            if GM > 0:
+                band = GM * n_tiles
+                bnd = L // band
+                first_m = bnd * GM
+                gm = min(m_used - first_m, GM)
+                rem = L - bnd * band
+                mt, nt = first_m + rem % gm, rem // gm
+            else:
+                r = L // n_tiles
+                e = int(np.searchsorted(offsets, r * BM, side="right") - 1)
+                first, rt = int(offsets[e]) // BM, int(offsets[e + 1] - offsets[e]) // BM
+                bi = (r - first) // -GM
+                bfirst = first + bi * -GM
+                gm = min(-GM, rt - bi * -GM)
+                local = L - bfirst * n_tiles
+                mt, nt = bfirst + local % gm, local // gm
             row0 = mt * BM
             if row0 >= offsets[E]:
                 continue

@@ -370,7 +370,9 @@ def test_layer_forward(name):
     dict(S=5, d=256, d_ff=512, E=256, K=8, n_groups=8, topk_groups=2, w="fp8"),  # fp8, decode regime
     dict(S=1500, d=256, d_ff=384, E=8, K=2),                       # prefill regime, ragged tiles
     dict(S=333, d=128, d_ff=256, E=32, K=3, act="f32", w="f32"),   # fp32 path
-    dict(S=64, d=512, d_ff=256, E=128, K=4, w="fp8"),              # mid regime fp8
+    dict(S=64, d=512, d_ff=256, E=128, K=4, w="fp8"),              # fp8, decode regime (2 rows per expert)
+    dict(S=600, d=256, d_ff=320, E=8, K=2, w="fp8"),               # fp8 mid regime: 128 x 64 up tiles (320 % 128)
+    dict(S=700, d=384, d_ff=512, E=8, K=2, w="fp8", router_offset="normal", offset_beta=1.5),  # fp8 mid, skewed
     dict(S=200, d=128, d_ff=128, E=512, K=8, n_groups=16, topk_groups=4),  # largest E, 16 groups
     dict(S=24, d=128, d_ff=128, E=128, K=64),                      # largest K
 ])

@@ -23,9 +23,24 @@ from tests.gpu_common import (DEV, GATE_TOL, TOL, act_from_raw, gpu_inputs, host
 
 pytestmark = pytest.mark.gpu
 
-# tile shape of the general kernel for 64-255 rows per expert: 128 x 256,
-# bands of 2 row tiles; BK = 64 with bf16 activations, 128 with e4m3 ones
-BM, BN, GM = 128, 256, 2
+# Tile shape (BM, BN, BK, GM) of the general kernel for 64-255 rows per
+# expert and a contraction of K: 128 x 256 tiles in expert-aligned bands of up
+# to 4 row tiles (GM = -4); k stages of 64 with bf16 weights, of 128 with fp8
+# weights when K % 128 == 0 (and always with e4m3 activations).
+BM = 128
+
+
+def tile_shape(w, K, a8=False):
+    fp8_k128 = a8 or (w == "fp8" and K % 128 == 0)
+    return BM, 256, 128 if fp8_k128 else 64, -4
+
+
+def split_tails(cfg, offsets, cap, a8=False):
+    """Split tail tiles of (the up product, the down product)."""
+    _, BN, BKu, GM = tile_shape(cfg.w, cfg.d, a8)
+    BKd = tile_shape(cfg.w, cfg.d_ff, a8)[2]
+    return (split_tail_tiles(offsets, cap, cfg.d_ff, cfg.d, BM, BN, BKu, GM),
+            split_tail_tiles(offsets, cap, cfg.d, cfg.d_ff, BM, BN, BKd, GM))
 
 
 def sync():
@@ -99,9 +114,7 @@ def _products(cfg, inp, ov):
     assert torch.equal(h[vi], h2[vi]) and torch.equal(y[vi], y2[vi])
     _split_vs_plain(h, h0, rows)
     _split_vs_plain(y, y0, rows)
-    tails = (split_tail_tiles(pm["offsets"], cap, cfg.d_ff, cfg.d, BM, BN, 64, GM),
-             split_tail_tiles(pm["offsets"], cap, cfg.d, cfg.d_ff, BM, BN, 64, GM))
-    return idx, pm, h, y, tails
+    return idx, pm, h, y, split_tails(cfg, pm["offsets"], cap)
 
 
 def test_dsv3_w8a16_split_tail_experts_every_row():
@@ -182,24 +195,22 @@ def test_w8a8_mid_regime_split_tail_all_tokens():
     p, y, idx, gate, lg, counts = _w8a8_layer(cfg, inp, None)
     assert M.moe_tile_m(p) == BM
     offs = np.concatenate([[0], np.cumsum(-(-counts // BM) * BM)])
-    cap = M.moe_rows_capacity(p)
-    assert split_tail_tiles(offs, cap, cfg.d_ff, cfg.d, BM, BN, 128, GM), "split tail tiles in the up product"
-    assert split_tail_tiles(offs, cap, cfg.d, cfg.d_ff, BM, BN, 128, GM), "split tail tiles in the down product"
+    up_tails, down_tails = split_tails(cfg, offs, M.moe_rows_capacity(p), a8=True)
+    assert up_tails, "split tail tiles in the up product"
+    assert down_tails, "split tail tiles in the down product"
     _w8a8_check(cfg, inp, np.arange(cfg.S), y, idx, gate, lg)
 
 
 def test_w8a8_dsv3_split_tail_tokens():
     """DeepSeek shape with fp8 activations: 64 tokens, 40 of them routed to
-    experts that own a split tail tile (of the up product: the down product's
-    last rounds are whole at this shape), the rest spread over the batch,
+    experts that own a split tail tile, the rest spread over the batch,
     against the oracle's W8A8 layer on the GPU's own scores."""
     cfg = D.CONFIGS["dsv3_fp8"]
     inp = gpu_inputs("dsv3_fp8")
     p, y, idx, gate, lg, counts = _w8a8_layer(cfg, inp, None)
     offs = np.concatenate([[0], np.cumsum(-(-counts // BM) * BM)])
-    cap = M.moe_rows_capacity(p)
-    tails = (split_tail_tiles(offs, cap, cfg.d_ff, cfg.d, BM, BN, 128, GM)
-             + split_tail_tiles(offs, cap, cfg.d, cfg.d_ff, BM, BN, 128, GM))
+    up_tails, down_tails = split_tails(cfg, offs, M.moe_rows_capacity(p), a8=True)
+    tails = up_tails + down_tails
     assert tails
     owners = sorted(set(e for _, _, e in tails))
     rng = np.random.default_rng(5)
@@ -215,7 +226,7 @@ def test_dsv3_w8a8_products_split_tail_experts_every_row():
     """The W8A8 stage entry points at the DeepSeek shape: x_perm quantised
     per row, the up product with the split tail against the unsplit launch on
     every valid row, h quantised per row, the same for the down product; and
-    every row of each expert owning a split tile (BK = 128) plus 16 spread
+    every row of each expert owning a split tile plus 16 spread
     experts against the oracle's W8A8 expert FFN."""
     cfg = D.CONFIGS["dsv3_fp8"]
     inp = gpu_inputs("dsv3_fp8")
@@ -246,8 +257,7 @@ def test_dsv3_w8a8_products_split_tail_experts_every_row():
     assert torch.equal(h[vi], h2[vi]) and torch.equal(y[vi], y2[vi])
     _split_vs_plain(h, h0, rows)
     _split_vs_plain(y, y0, rows)
-    up_tails = split_tail_tiles(pm["offsets"], cap, cfg.d_ff, cfg.d, BM, BN, 128, GM)
-    down_tails = split_tail_tiles(pm["offsets"], cap, cfg.d, cfg.d_ff, BM, BN, 128, GM)
+    up_tails, down_tails = split_tails(cfg, pm["offsets"], cap, a8=True)
     assert up_tails
     owners = sorted(set(e for _, _, e in up_tails + down_tails))
     spread = [int(e) for e in np.linspace(0, cfg.E - 1, 16).round()]
