@@ -20,11 +20,11 @@ hipError_t launch_route_logits(const Problem&, const float*, const float*, float
 hipError_t launch_router_gemm(const Problem&, const void*, const void*, const float*, float*,
                               hipStream_t);
 hipError_t launch_permute(const Problem&, int, const int32_t*, const void*, int32_t*, int32_t*,
-                          int32_t*, int32_t*, void*, int32_t*, hipStream_t);
+                          int32_t*, int32_t*, void*, int32_t*, hipStream_t, int32_t*);
 size_t permute_scratch_ints(int64_t pairs, int E);
 hipError_t launch_expert_up(const Problem&, int64_t, const void*, const int32_t*, const int32_t*,
                             const void*, const void*, const float*, void*, float*, size_t,
-                            hipStream_t, const float*);
+                            hipStream_t, const float*, const int32_t*);
 hipError_t launch_expert_down(const Problem&, int64_t, const void*, const int32_t*,
                               const int32_t*, const void*, const void*, const float*, void*,
                               float*, size_t, hipStream_t, const float*);
@@ -39,6 +39,7 @@ hipError_t launch_capacity(const Problem&, int, const float*, const float*, int3
                            int32_t*, int32_t*, hipStream_t);
 size_t capacity_scratch_ints(int64_t pairs, int E);
 int gemm_tile_m(const Problem& p);
+bool expert_up_reads_in_place(const Problem& p);
 }  // namespace sfl
 
 using namespace sfl;
@@ -108,6 +109,15 @@ int64_t rows_capacity(const Problem& p) {
   return pairs + (pairs < p.E ? pairs : p.E) * (tm - 1);
 }
 
+// The layer's up product reads the token rows of x (or, W8A8, their e4m3
+// codes) in place through a row -> token map written by the permute, instead
+// of a gathered x_perm, when its kernel can (bf16 activations, not the
+// four-wave prefill kernel) and the source fits one 32-bit buffer range.
+bool in_place_rows(const Problem& p) {
+  const int64_t asz = p.act_quant ? 1 : 2;
+  return expert_up_reads_in_place(p) && (p.S + 1) * (int64_t)p.d * asz < (int64_t(1) << 32);
+}
+
 size_t route_ws(const Problem& p) { return uses_router_gemm(p) ? align_up((size_t)p.S * p.E * 4) : 0; }
 size_t permute_ws(const Problem& p) { return align_up(permute_scratch_ints(p.S * p.K, p.E) * 4); }
 size_t capacity_ws(const Problem& p) { return align_up(capacity_scratch_ints(p.S * p.K, p.E) * 4); }
@@ -116,6 +126,7 @@ size_t capacity_ws(const Problem& p) { return align_up(capacity_scratch_ints(p.S
 struct LayerWs {
   float* logits; int32_t* idx; float* gate; int32_t* counts; int32_t* offsets;
   int32_t* perm; int32_t* inv; int32_t* pscratch; int32_t* cscratch; void* x_perm; void* h; void* y_perm;
+  int32_t* row_tok;  // rows read in place: the token of every row of the expert groups
   uint8_t* h8; float* xs; float* hs;  // fp8 activations: h codes, row scales of x_perm and h
   float* split; size_t split_bytes;
   size_t bytes;
@@ -134,12 +145,18 @@ LayerWs layer_layout(const Problem& p, char* base) {
   w.inv = (int32_t*)take((size_t)pairs * 4);
   w.pscratch = (int32_t*)take(permute_scratch_ints(pairs, p.E) * 4);
   w.cscratch = p.capacity > 0 ? (int32_t*)take(capacity_scratch_ints(pairs, p.E) * 4) : nullptr;
-  w.x_perm = take((size_t)cap * p.d * act_size(p));
+  // x_perm holds the gathered rows, or with fp8 activations their e4m3 codes
+  // (one row per token when the rows are read in place); it is not needed
+  // for bf16 rows read in place
+  const bool inplace = in_place_rows(p);
+  const int64_t xrows = inplace ? (p.act_quant ? p.S : 0) : cap;
+  w.row_tok = inplace ? (int32_t*)take((size_t)cap * 4) : nullptr;
+  w.x_perm = take((size_t)xrows * p.d * (p.act_quant ? 1 : act_size(p)));
   w.h = take((size_t)cap * p.d_ff * act_size(p));
   w.y_perm = take((size_t)cap * p.d * act_size(p));
-  if (p.act_quant) {  // x_perm then holds the e4m3 codes of x (fewer bytes than bf16)
+  if (p.act_quant) {
     w.h8 = (uint8_t*)take((size_t)cap * p.d_ff);
-    w.xs = (float*)take((size_t)cap * 4);
+    w.xs = (float*)take((size_t)xrows * 4);
     w.hs = (float*)take((size_t)cap * 4);
   }
   w.split_bytes = expert_split_bytes(p);
@@ -151,14 +168,15 @@ LayerWs layer_layout(const Problem& p, char* base) {
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // split: float32 workspace for the split-K tail (nullable; then no split).
+// row_tok (nullable): x_perm is x itself, read in place through this map.
 int32_t do_expert_ffn(const Problem& p, const void* x_perm, const int32_t* counts,
                       const int32_t* offsets, const void* W1, const void* b1, const void* W2,
                       const void* b2, const float* s1, const float* s2, void* h, void* y_perm,
-                      float* split, size_t split_bytes, hipStream_t st) {
+                      float* split, size_t split_bytes, hipStream_t st, const int32_t* row_tok = nullptr) {
   const bool fp8 = p.w == DT_FP8;
   const int64_t cap = rows_capacity(p);
   int32_t s = hip_status(launch_expert_up(p, cap, x_perm, counts, offsets, W1, b1, fp8 ? s1 : nullptr,
-                                          h, split, split_bytes, st, nullptr));
+                                          h, split, split_bytes, st, nullptr, row_tok));
   if (s != MOE_OK) return s;
   return hip_status(launch_expert_down(p, cap, h, counts, offsets, W2, b2, fp8 ? s2 : nullptr,
                                        y_perm, split, split_bytes, st, nullptr));
@@ -241,19 +259,24 @@ int32_t layer_run(const moe_problem* mp, const LayerArgs& a, void* ws, hipStream
     s = hip_status(launch_capacity(p, p.capacity, lg, a.select_bias, idx, gate, nullptr, w.cscratch, st));
     if (s != MOE_OK) return s;
   }
+  const bool inplace = in_place_rows(p);
   if (p.act_quant) {
-    // W8A8: the gather writes e4m3 rows and row scales; h is quantised per
+    // W8A8: e4m3 rows and row scales of x -- one per token, read in place by
+    // the up product, or gathered per (token, slot) pair; h is quantised per
     // row between the two products
     const int64_t pairs = p.S * p.K, cap = rows_capacity(p);
     uint8_t* x8 = (uint8_t*)w.x_perm;
     s = hip_status(launch_permute(p, gemm_tile_m(p), idx, a.x, counts, w.offsets, w.perm, w.inv, nullptr,
-                                  w.pscratch, st));
+                                  w.pscratch, st, w.row_tok));
     if (s != MOE_OK) return s;
-    s = hip_status(launch_quantize_rows((const uint16_t*)a.x, p.d, p.d, pairs, p.K, true, w.inv, x8, p.d, w.xs,
-                                        st));
+    if (inplace)
+      s = hip_status(launch_quantize_rows((const uint16_t*)a.x, p.d, p.d, p.S, 1, false, nullptr, x8, p.d, w.xs, st));
+    else
+      s = hip_status(launch_quantize_rows((const uint16_t*)a.x, p.d, p.d, pairs, p.K, true, w.inv, x8, p.d, w.xs,
+                                          st));
     if (s != MOE_OK) return s;
     s = hip_status(launch_expert_up(p, cap, x8, counts, w.offsets, a.W1, a.b1, a.w1_scale, w.h, w.split,
-                                    w.split_bytes, st, w.xs));
+                                    w.split_bytes, st, w.xs, w.row_tok));
     if (s != MOE_OK) return s;
     s = hip_status(launch_quantize_rows((const uint16_t*)w.h, p.d_ff, p.d_ff, pairs, p.K, false, w.inv, w.h8,
                                         p.d_ff, w.hs, st));
@@ -264,10 +287,10 @@ int32_t layer_run(const moe_problem* mp, const LayerArgs& a, void* ws, hipStream
     return hip_status(launch_combine(p, w.y_perm, w.inv, gate, a.y, st));
   }
   s = hip_status(launch_permute(p, gemm_tile_m(p), idx, a.x, counts, w.offsets, w.perm, w.inv,
-                                w.x_perm, w.pscratch, st));
+                                inplace ? nullptr : w.x_perm, w.pscratch, st, w.row_tok));
   if (s != MOE_OK) return s;
-  s = do_expert_ffn(p, w.x_perm, counts, w.offsets, a.W1, a.b1, a.W2, a.b2, a.w1_scale, a.w2_scale, w.h,
-                    w.y_perm, w.split, w.split_bytes, st);
+  s = do_expert_ffn(p, inplace ? a.x : w.x_perm, counts, w.offsets, a.W1, a.b1, a.W2, a.b2, a.w1_scale,
+                    a.w2_scale, w.h, w.y_perm, w.split, w.split_bytes, st, w.row_tok);
   if (s != MOE_OK) return s;
   return hip_status(launch_combine(p, w.y_perm, w.inv, gate, a.y, st));
 }
@@ -345,7 +368,7 @@ int32_t moe_permute(const moe_problem* mp, const int32_t* topk_idx, const void* 
     if (q == nullptr || !aligned16(q)) return MOE_ERR_INVALID_ARG;
   if (ws == nullptr || ws_bytes < permute_ws(p)) return MOE_ERR_WORKSPACE;
   return hip_status(launch_permute(p, gemm_tile_m(p), topk_idx, x, expert_counts, expert_offsets,
-                                   perm, inv_perm, x_perm, (int32_t*)ws, (hipStream_t)stream));
+                                   perm, inv_perm, x_perm, (int32_t*)ws, (hipStream_t)stream, nullptr));
 }
 
 int32_t moe_expert_ffn(const moe_problem* mp, const void* x_perm, const int32_t* expert_counts,
@@ -375,7 +398,7 @@ int32_t moe_expert_up(const moe_problem* mp, const void* x_perm, const int32_t* 
   float* split = split_region(ws, ws_bytes, &usable);
   return hip_status(launch_expert_up(p, rows_capacity(p), x_perm, expert_counts, expert_offsets, W1,
                                      b1, p.w == DT_FP8 ? w1_scale : nullptr, h, split, usable,
-                                     (hipStream_t)stream, nullptr));
+                                     (hipStream_t)stream, nullptr, nullptr));
 }
 
 int32_t moe_expert_down(const moe_problem* mp, const void* h, const int32_t* expert_counts,
@@ -412,7 +435,7 @@ int32_t moe_expert_up_a8(const moe_problem* mp, const uint8_t* x8, const float* 
   size_t usable = 0;
   float* split = split_region(ws, ws_bytes, &usable);
   return hip_status(launch_expert_up(p, rows_capacity(p), x8, expert_counts, expert_offsets, W1, b1, w1_scale,
-                                     h, split, usable, (hipStream_t)stream, x_scale));
+                                     h, split, usable, (hipStream_t)stream, x_scale, nullptr));
 }
 
 int32_t moe_expert_down_a8(const moe_problem* mp, const uint8_t* h8, const float* h_scale,

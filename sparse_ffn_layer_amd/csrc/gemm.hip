@@ -68,6 +68,12 @@ struct GemmArgs {
   int m_tiles, n_tiles;  // m_tiles: upper bound (capacity / BM)
   float* partial;        // split-K partial sums of the tail tiles ([grid][BM*BN] floats) or null
   int grid;              // workgroups of the persistent launch
+  // Rows read in place (nullable): row r of the product reads row a_rows[r]
+  // of A, an array of a_src_rows rows (the token rows of x, for instance,
+  // in place of a gathered copy); its byte size must stay below 2^32 - lda.
+  // Row scales of e4m3 activations are then those of the source rows.
+  const int32_t* a_rows;
+  int64_t a_src_rows;
 };
 
 // Tail split of one XCD's tile range.  The tile space is cut into 8 slices
@@ -242,7 +248,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const acc_t (&a
         if (wm * WTM + i * MF >= rows) continue;  // uniform: fragment wholly past the rows
         const int m = wm * WTM + i * MF + lr;
         if (m < rows) {
-          const float rs = A8 ? a.a_scale[row0 + m] : 1.f;
+          const float rs = A8 ? a.a_scale[a.a_rows != nullptr ? (int64_t)a.a_rows[row0 + m] : row0 + m] : 1.f;
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -265,6 +271,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const acc_t (&a
   }
 }
 
+// Tile shapes of the general kernel that can read rows in place.
+constexpr bool in_place_tiles(int BM, int BN) { return !(BM == 256 && BN == 256); }
+
 // MF selects the MFMA: 16 (v_mfma_f32_16x16x32_bf16) or 32
 // (v_mfma_f32_32x32x16_bf16).  Operand lanes: row (lane % MF) of the
 // fragment, 8 consecutive k values starting at 8 * (lane / MF).  Result
@@ -275,7 +284,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const acc_t (&a
 // form with unit scales); each lane supplies 32 codes of its row for both
 // operands, taken from the same k positions, so the products pair up
 // whatever order the hardware reads the 32 bytes in.
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF, bool A8 = false>
+// INP: the rows are read in place (a.a_rows, the up product of the layer);
+// a separate instance, so that the other launches keep their registers.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF, bool A8 = false,
+          bool INP = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_bf16_kernel(const GemmArgs a) {
   static_assert(!A8 || BFP8, "e4m3 activations go with e4m3 weights");
@@ -299,6 +311,10 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   constexpr int RD = A8 ? 2 : 1;             // 16-byte LDS reads per fragment
   typedef typename std::conditional<MF == 16, f32x4_t, f32x16_t>::type acc_t;
   typedef typename std::conditional<A8, i32x8_t, bf16x8_t>::type frag_t;
+  // Rows read in place (a.a_rows) keep per-tile A offsets in the work items;
+  // the 256 x 256 tiles have no registers left for them.
+  constexpr bool IN_PLACE = INP;
+  static_assert(!INP || in_place_tiles(BM, BN), "tile shape without rows read in place");
   // Large wave tiles keep their accumulators in AGPRs (MFMAs issued as
   // inline asm with AGPR operands), leaving the VGPRs to the fragments.
   constexpr bool AGPR_ACC = MF == 32 && !BFP8 && FM * FN * NACC > 128;
@@ -340,14 +356,32 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   // into the scalar offset.  The resources cover exactly the tile's valid
   // rows (num_records in bytes), so chunks of rows past the group's count
   // are dropped by the buffer range check: no memory access, zeros in LDS,
-  // and those rows are never stored.  Every access stays inside the
-  // operands by construction.
+  // and those rows are never stored.  With rows read in place (a.a_rows),
+  // the A resource covers the whole source and each chunk's offset comes
+  // from its row's source row; rows past the count get the offset
+  // num_records, which the range check drops the same way.  Every access
+  // stays inside the operands by construction.
   struct Item {
     int64_t row0;
     int n0, g, rows, kt0, kt1;
     float* part;     // split-K slice: raw float32 accumulators go here
     i32x4_t ra, rb;  // buffer resources of the tile's A rows and B rows
+    uint32_t aoff[IN_PLACE ? A_LOADS : 1];  // this thread's A chunk offsets in ra (rows read in place)
   };
+  // per-thread chunk offsets inside a tile (the same for every tile)
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int q = i * NT + tid;
+    const int r = q / CA, s = q % CA;
+    a_off[i] = (uint32_t)(r * a.lda * ASZ + (s ^ swz<CA>(r)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int q = i * NT + tid;
+    const int r = q / CB, s = q % CB;
+    b_off[i] = (uint32_t)(r * a.ldb * BSZ + (s ^ swz<CB>(r)) * 16);
+  }
   const int64_t loop_end = tp.split ? tp.full_end : tp.t_hi;
   const bool has_slice = tp.split && xj < tp.tail * tp.split;
   // the first valid item at tile index >= L (L is advanced past it)
@@ -370,34 +404,33 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
         return i32x4_t{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
                        __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w)};
       };
-      it.ra = uni(make_rsrc((const char*)a.A + it.row0 * a.lda * ASZ, (uint32_t)((int64_t)it.rows * a.lda * ASZ)));
+      if constexpr (!IN_PLACE) {
+        it.ra = uni(make_rsrc((const char*)a.A + it.row0 * a.lda * ASZ, (uint32_t)((int64_t)it.rows * a.lda * ASZ)));
+      } else {
+        const uint32_t nrec = (uint32_t)(a.a_src_rows * a.lda * ASZ);
+        it.ra = uni(make_rsrc(a.A, nrec));
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) {
+          const int q = i * NT + tid;
+          const int r = q / CA, s = q % CA;
+          it.aoff[i] = r < it.rows ? (uint32_t)((int64_t)a.a_rows[it.row0 + r] * a.lda * ASZ + (s ^ swz<CA>(r)) * 16)
+                                   : nrec;
+        }
+      }
       it.rb = uni(make_rsrc((const char*)a.B + (int64_t)it.g * a.b_gstride * BSZ + (int64_t)it.n0 * a.ldb * BSZ,
                             (uint32_t)((int64_t)BN * a.ldb * BSZ)));
       L += nx;
       return true;
     }
   };
-  // per-thread chunk offsets (the same for every tile)
-  uint32_t a_off[A_LOADS], b_off[B_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int q = i * NT + tid;
-    const int r = q / CA, s = q % CA;
-    a_off[i] = (uint32_t)(r * a.lda * ASZ + (s ^ swz<CA>(r)) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int q = i * NT + tid;
-    const int r = q / CB, s = q % CB;
-    b_off[i] = (uint32_t)(r * a.ldb * BSZ + (s ^ swz<CB>(r)) * 16);
-  }
   // copy l of stage kt of item t into LDS slot `slot`: the A chunks first,
   // then the B chunks
   auto issue_one = [&](const Item& t, int kt, int slot, int l) {
     char* sa = smem + slot * STAGE_BYTES;
     char* sb = sa + A_BYTES;
     if (l < A_LOADS)
-      buffer_load_lds_16(t.ra, sa + (l * NT + wave * 64) * 16, a_off[l], (uint32_t)((t.kt0 + kt) * BK * ASZ));
+      buffer_load_lds_16(t.ra, sa + (l * NT + wave * 64) * 16, IN_PLACE ? t.aoff[IN_PLACE ? l : 0] : a_off[l],
+                         (uint32_t)((t.kt0 + kt) * BK * ASZ));
     else
       buffer_load_lds_16<B_AUX>(t.rb, sb + ((l - A_LOADS) * NT + wave * 64) * 16, b_off[l - A_LOADS],
                                 (uint32_t)((t.kt0 + kt) * BK * BSZ));
@@ -829,7 +862,8 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
   const TailPlan tp = tail_plan(T, xcd, nx, a.partial != nullptr && KT_ALL >= 16);
 
   // Work item k of this workgroup: whole tiles of the full rounds, then
-  // (with a split) one k-slice of a tail tile.
+  // (with a split) one k-slice of a tail tile.  (No rows read in place here:
+  // the item's offsets would not fit the registers this kernel has left.)
   struct Item {
     int64_t row0;
     int n0, g, rows, kt0, kt1;
@@ -1191,19 +1225,28 @@ constexpr int kSplitGrid = 512;
 // kernel reduces them.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF = 16, bool A8 = false>
 hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial_bytes = 0) {
-  auto kern = grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF, A8>;
+  auto kern = grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF, A8, false>;
   constexpr int NT = 64 * WM * WN;
+  if (a.a_rows != nullptr) {
+    // rows read in place: up products on tile shapes that keep the offsets
+    // (expert_up_reads_in_place chooses them; anything else is a caller bug)
+    if constexpr (EPI == EPI_GELU && in_place_tiles(BM, BN))
+      kern = grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF, A8, true>;
+    else
+      return hipErrorInvalidValue;
+  }
   a.m_tiles = (int)ceil_div(rows_cap, BM);
   a.n_tiles = a.N / BN;
   const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
   if (tiles == 0) return hipSuccess;
-  static int occ = 0;  // resident workgroups per CU (same for every gfx950 device)
-  if (occ == 0) {
+  static int occ[2] = {0, 0};  // resident workgroups per CU of each instance (same on every gfx950 device)
+  int& oc = occ[a.a_rows != nullptr];
+  if (oc == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NT, 0) != hipSuccess || n < 1) n = 1;
-    occ = n;
+    oc = n;
   }
-  int64_t grid = (int64_t)device_cus() * occ;
+  int64_t grid = (int64_t)device_cus() * oc;
   if (grid > tiles) grid = tiles;
   grid = grid < 8 ? 8 : grid / 8 * 8;
   a.grid = (int)grid;
@@ -1229,6 +1272,7 @@ hipError_t run_bf16_w4(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t part
   grid = grid < 8 ? 8 : grid / 8 * 8;
   a.grid = (int)grid;
   if (a.partial != nullptr && (size_t)grid * 256 * 256 * sizeof(float) > partial_bytes) a.partial = nullptr;
+  if (a.a_rows != nullptr) return hipErrorInvalidValue;  // no rows read in place here
   hipLaunchKernelGGL(grouped_gemm_bf16_w4_kernel<EPI>, dim3((unsigned)grid), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partial == nullptr) return e;
@@ -1249,6 +1293,16 @@ static hipError_t run_f32(GemmArgs a, int64_t rows_cap, hipStream_t st) {
 
 // Tile shapes per regime.  BN must divide N and BK must divide K; both are
 // multiples of 64, so the wider variants fall back when needed.
+// Whether the up product of problem p (N = d_ff, K = d) runs on a kernel
+// that reads rows in place (a_rows): the choices of run_regime and
+// run_regime_a8 below, minus the four-wave kernel and the 256 x 256 tiles of
+// the general one (their launchers refuse a_rows), and the fp32 kernel.
+bool expert_up_reads_in_place(const Problem& p) {
+  if (p.act != DT_BF16) return false;
+  if (p.act_quant || gemm_regime(p) != 0) return true;
+  return p.d_ff % 256 != 0;  // prefill: 256 x 256 tiles (four-wave for bf16 weights) unless N % 256 != 0
+}
+
 template <bool BFP8, int EPI>
 static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hipStream_t st, size_t pb) {
   const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0, k128 = a.K % 128 == 0;
@@ -1321,12 +1375,18 @@ static hipError_t run_expert_gemm(const Problem& p, const GemmArgs& g, int64_t r
 
 // h = GeLU(x_perm W1^T + b1) over the expert groups.
 // a_scale: row scales of e4m3 activations (W8A8), or null for bf16 rows.
+// row_tok (nullable): read the rows in place, row r of the groups from row
+// row_tok[r] of x_perm (then the token rows of x, S of them, or their e4m3
+// codes with a_scale per token) instead of a gathered copy.
 hipError_t launch_expert_up(const Problem& p, int64_t rows_cap, const void* x_perm,
                             const int32_t* counts, const int32_t* offsets, const void* W1,
                             const void* b1, const float* s1, void* h, float* partial,
-                            size_t partial_bytes, hipStream_t st, const float* a_scale) {
+                            size_t partial_bytes, hipStream_t st, const float* a_scale,
+                            const int32_t* row_tok) {
   GemmArgs g = expert_args(p, counts, offsets);
   g.a_scale = a_scale;
+  g.a_rows = row_tok;
+  g.a_src_rows = p.S;
   g.partial = partial;
   g.A = x_perm; g.lda = p.d;
   g.B = W1; g.ldb = p.d; g.b_gstride = (int64_t)p.d_ff * p.d;

@@ -18,7 +18,9 @@
 //   3. scatter: each block ranks its pairs in order (wave ballots give the
 //               rank among equal experts inside a wave, LDS counters carry
 //               the rank across waves and rounds) and writes perm/inv_perm.
-//   4. gather:  x_perm[inv_perm[p]] = x[p / K], one wave per row.
+//   4. gather:  x_perm[inv_perm[p]] = x[p / K], one wave per row; or, for a
+//               product that reads the token rows of x itself, the row ->
+//               token map row_tok[inv_perm[p]] = p / K written in step 3.
 // When all pairs fit one block, steps 1-3 run as one single-block kernel.
 #include "common.h"
 
@@ -118,7 +120,8 @@ __global__ void __launch_bounds__(PERM_THREADS)
 permute_scatter_kernel(const int32_t* __restrict__ idx, int64_t pairs, int E, int ebits,
                        int64_t chunk, const int32_t* __restrict__ base,
                        const int32_t* __restrict__ dense, const int32_t* __restrict__ offsets,
-                       int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+                       int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, int K,
+                       int32_t* __restrict__ row_tok) {
   __shared__ int run[PERM_MAX_E];
   __shared__ int wc[PERM_THREADS / 64][PERM_MAX_E + 1];
   const int nb = gridDim.x, b = blockIdx.x;
@@ -153,6 +156,7 @@ permute_scatter_kernel(const int32_t* __restrict__ idx, int64_t pairs, int E, in
       for (int w = 0; w < wave; ++w) pos += wc[w][e];
       perm[dense[e] + pos] = (int32_t)p;
       inv_perm[p] = offsets[e] + pos;
+      if (row_tok != nullptr) row_tok[offsets[e] + pos] = (int32_t)(p / K);
     }
     __syncthreads();
     if (valid && leader) {
@@ -169,7 +173,8 @@ permute_scatter_kernel(const int32_t* __restrict__ idx, int64_t pairs, int E, in
 __global__ void __launch_bounds__(PERM_THREADS)
 permute_single_kernel(const int32_t* __restrict__ idx, int64_t pairs, int E, int ebits, int tile_m,
                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                      int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+                      int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, int K,
+                      int32_t* __restrict__ row_tok) {
   __shared__ int run[PERM_MAX_E];
   __shared__ int dns[PERM_MAX_E];
   __shared__ int ofs[PERM_MAX_E];
@@ -237,6 +242,7 @@ permute_single_kernel(const int32_t* __restrict__ idx, int64_t pairs, int E, int
       for (int w = 0; w < wave; ++w) pos += wc[w][e];
       perm[dns[e] + pos] = (int32_t)p;
       inv_perm[p] = ofs[e] + pos;
+      if (row_tok != nullptr) row_tok[ofs[e] + pos] = (int32_t)(p / K);
     }
     __syncthreads();
     if (valid && leader) {
@@ -266,9 +272,12 @@ size_t permute_scratch_ints(int64_t pairs, int E) {
   return (size_t)E * permute_blocks(pairs, E) + (size_t)E + 1;
 }
 
+// row_tok (nullable): also write, for every row of the expert groups, the
+// token it holds (row_tok[inv_perm[p]] = p / K), so that a product can read
+// the token rows of x in place of a gathered x_perm.
 hipError_t launch_permute(const Problem& p, int tile_m, const int32_t* idx, const void* x,
                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                          void* x_perm, int32_t* scratch, hipStream_t st) {
+                          void* x_perm, int32_t* scratch, hipStream_t st, int32_t* row_tok) {
   const int64_t pairs = p.S * p.K;
   const int nb = permute_blocks(pairs, p.E);
   const int64_t chunk = ceil_div(pairs, nb);
@@ -280,7 +289,7 @@ hipError_t launch_permute(const Problem& p, int tile_m, const int32_t* idx, cons
   hipError_t err;
   if (nb == 1) {
     permute_single_kernel<<<1, PERM_THREADS, 0, st>>>(idx, pairs, p.E, ebits, tile_m, counts, offsets, perm,
-                                                      inv_perm);
+                                                      inv_perm, p.K, row_tok);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   } else {
     permute_count_kernel<<<nb, PERM_THREADS, 0, st>>>(idx, pairs, p.E, chunk, hist);
@@ -289,7 +298,7 @@ hipError_t launch_permute(const Problem& p, int tile_m, const int32_t* idx, cons
     permute_scan_kernel<<<1, SCAN_THREADS, lds, st>>>(p.E, nb, tile_m, hist, counts, dense, offsets);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     permute_scatter_kernel<<<nb, PERM_THREADS, 0, st>>>(idx, pairs, p.E, ebits, chunk, hist, dense,
-                                                       offsets, perm, inv_perm);
+                                                       offsets, perm, inv_perm, p.K, row_tok);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (x_perm != nullptr) {

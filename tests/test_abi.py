@@ -229,7 +229,7 @@ def test_capacity_formula(S, E, K):
     assert M.moe_rows_capacity(p) == pairs + min(E, pairs) * (tm - 1)
     cap = M.moe_rows_capacity(p)
     ws = M.moe_workspace_bytes(p, M.STAGE_LAYER)
-    assert ws >= cap * (2 * 4096 + 14336) * 2
+    assert ws >= cap * (4096 + 14336) * 2   # h and y_perm (x_perm only when rows are not read in place)
 
 
 def test_apply_capacity_argument_checks():
