@@ -1422,7 +1422,11 @@ hipError_t launch_router_gemm(const Problem& p, const void* x, const void* Wr, c
   a.C = logits; a.ldc = p.E;
   a.M = p.S; a.G = 1;
   a.N = p.E; a.K = p.d;
-  return run_bf16<128, 64, 64, 4, 1, 3, false, EPI_F32, 8>(a, p.S, st);
+  // the largest row tile that still gives every compute unit a tile
+  const int64_t nt = p.E / 64, cus = device_cus();
+  if (ceil_div(p.S, 128) * nt >= cus) return run_bf16<128, 64, 64, 4, 1, 3, false, EPI_F32, 8>(a, p.S, st);
+  if (ceil_div(p.S, 64) * nt >= cus) return run_bf16<64, 64, 64, 2, 2, 3, false, EPI_F32, 8>(a, p.S, st);
+  return run_bf16<32, 64, 64, 2, 2, 3, false, EPI_F32, 8>(a, p.S, st);
 }
 
 }  // namespace sfl
