@@ -156,9 +156,15 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 //  sit in the tile space exactly where their row tiles are (row tile r
 //  covers positions [r n_tiles, (r + 1) n_tiles)), so tile L finds its band
 //  with the same binary search over the offsets that finds its expert.
-template <int BM, int BN, int GM>
+//  FR > 0 (GM < 0 only): balanced row tiles: the expert's rows, in blocks of
+//  FR (the MFMA fragment), are dealt evenly over its row tiles instead of
+//  filling them in order (129 rows on 128-row tiles: 96 + 33 rather than
+//  128 + 1), so the tiles sharing a weight panel do the same work and stay
+//  in step, and the panel read by one is still in L2 for the other.
+template <int BM, int BN, int GM, int FR = 0>
 __device__ __forceinline__ bool tile_coords(const GemmArgs& a, int m_used, int64_t L, int64_t& row0, int& n0,
                                             int& g, int& rows) {
+  static_assert(FR == 0 || (GM < 0 && BM % FR == 0), "balanced row tiles: expert-aligned bands, whole fragments");
   if constexpr (GM < 0) {
     if (a.offsets == nullptr) return tile_coords<BM, BN, 1>(a, m_used, L, row0, n0, g, rows);
     constexpr int GB = -GM;
@@ -175,9 +181,21 @@ __device__ __forceinline__ bool tile_coords(const GemmArgs& a, int m_used, int64
     const int bfirst = first + bi * GB;
     const int gm = rt - bi * GB < GB ? rt - bi * GB : GB;
     const int64_t local = L - (int64_t)bfirst * a.n_tiles;
-    row0 = (int64_t)(bfirst + (int)(local % gm)) * BM;
+    const int t = bfirst - first + (int)(local % gm);  // row tile of the expert
     n0 = (int)(local / gm) * BN;
     g = lo;
+    if constexpr (FR > 0) {
+      // rt = ceil(count / BM) tiles share ceil(count / FR) >= rt fragments:
+      // tile t gets q or q + 1 (<= BM / FR) of them, at least one row each
+      const int frags = (a.counts[g] + FR - 1) / FR;
+      const int q = frags / rt, rem = frags % rt;
+      const int f0 = t * q + (t < rem ? t : rem), nf = q + (t < rem ? 1 : 0);
+      row0 = (int64_t)a.offsets[g] + (int64_t)f0 * FR;
+      const int left = a.counts[g] - f0 * FR;
+      rows = left < nf * FR ? left : nf * FR;
+      return rows > 0;
+    }
+    row0 = (int64_t)(first + t) * BM;
     const int64_t left = a.counts[g] - (row0 - a.offsets[g]);
     rows = (int)(left < BM ? left : BM);
     return rows > 0;
@@ -319,6 +337,9 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   // inline asm with AGPR operands), leaving the VGPRs to the fragments.
   constexpr bool AGPR_ACC = MF == 32 && !BFP8 && FM * FN * NACC > 128;
   static_assert(KS >= 1 && BK % KSTEP == 0, "whole MFMA k-steps per stage");
+  // Expert-aligned bands deal each expert's rows evenly over its row tiles
+  // (in whole MFMA fragments).
+  constexpr int BAL_FR = GM < 0 ? MF : 0;
   // Decode tiles (a few rows per expert) read every weight exactly once:
   // those loads are marked non-temporal.
   constexpr int B_AUX = BM <= 16 ? 2 : 0;
@@ -399,7 +420,7 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
         it.kt1 = KT_ALL * (sig + 1) / tp.split;
         it.part = a.partial + (size_t)blockIdx.x * (BM * BN);
       }
-      if (!tile_coords<BM, BN, GM>(a, m_used, Lt, it.row0, it.n0, it.g, it.rows)) continue;
+      if (!tile_coords<BM, BN, GM, BAL_FR>(a, m_used, Lt, it.row0, it.n0, it.g, it.rows)) continue;
       auto uni = [](i32x4_t v) {
         return i32x4_t{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
                        __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w)};
@@ -645,10 +666,15 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
     using P0 = std::integral_constant<int, 0>;
     using PA1 = std::integral_constant<int, (KS & 1)>;
     using PB1 = std::integral_constant<int, PAIR ? ((KS / 2) & 1) : (KS & 1)>;
-    for (int kt = 0; kt < KT; kt += 2) {
+    // every item has at least one k stage; a loop that may run zero times
+    // would merge the zeroed accumulators with the loop's results (copies of
+    // every accumulator after it, and more registers in use)
+    int kt = 0;
+    do {
       stage(kt, P0{}, P0{});
       if (kt + 1 < KT) stage(kt + 1, PA1{}, PB1{});
-    }
+      kt += 2;
+    } while (kt < KT);
 
     if constexpr (AGPR_ACC) {
       // the last MFMAs wrote the accumulators (AGPRs) behind the compiler's
@@ -719,7 +745,8 @@ grouped_gemm_fixup_kernel(const GemmArgs a) {
   if (tp.split == 0 || tau >= tp.tail) return;
   int64_t row0;
   int n0, g, rows;
-  if (!tile_coords<BM, BN, GM>(a, m_used, tp.full_end + tau, row0, n0, g, rows)) return;
+  constexpr int BAL_FR = GM < 0 ? MF : 0;  // balanced row tiles, as in the GEMM
+  if (!tile_coords<BM, BN, GM, BAL_FR>(a, m_used, tp.full_end + tau, row0, n0, g, rows)) return;
   acc_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
