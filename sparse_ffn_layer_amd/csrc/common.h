@@ -98,42 +98,66 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 }
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
+// Eight bf16 values (one 16-byte chunk) times r, clamped, as e4m3 codes.
+__device__ __forceinline__ uint2 e4m3x8_scaled(uint4 raw, float r) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = clamp448(bf16_bits_to_f32(w[q] & 0xffff) * r);
+    v[2 * q + 1] = clamp448(bf16_bits_to_f32(w[q] >> 16) * r);
+  }
+  return make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7]));
+}
+__device__ __forceinline__ float chunk_amax(uint4 raw, float amax) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xffff)));
+    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
+  }
+  return amax;
+}
+
 // One row of n bf16 values (n % 8 == 0) -> e4m3 codes and one float32 scale,
 // by the whole wave:  amax = max |v|,  scale = amax / 448,  r = 448 / amax,
 // code = e4m3(clamp(v * r, -448, 448)); a row of zeros gets scale 0 and
 // codes 0.  Each quotient and product is one float32 operation, so the codes
-// are a function of the bf16 inputs alone.  A pass over the row for amax, a
-// second (from cache) for the codes: 16 bytes in, 8 bytes of codes out per
-// lane and step.
+// are a function of the bf16 inputs alone.  Rows of up to 512 R values are
+// read once, all of a lane's chunks in flight together, and held in
+// registers for the second step; longer rows are read twice (the second
+// time from cache).
+template <int R>
 __device__ __forceinline__ void wave_quantize_row_e4m3(const uint16_t* __restrict__ s, int n,
                                                        uint8_t* __restrict__ d, float* __restrict__ scale_out) {
   const int lane = lane_id();
-  float amax = 0.f;
-  for (int c = lane * 8; c < n; c += 64 * 8) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(s + c);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float amax = 0.f, scale, r;
+  if (n <= 64 * 8 * R) {
+    uint4 raw[R];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xffff)));
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
+    for (int i = 0; i < R; ++i) {
+      const int c = (i * 64 + lane) * 8;
+      raw[i] = c < n ? *reinterpret_cast<const uint4*>(s + c) : make_uint4(0, 0, 0, 0);
     }
-  }
-  amax = wave_max(amax);
-  const float scale = amax / 448.f;
-  const float r = amax > 0.f ? 448.f / amax : 0.f;
-  for (int c = lane * 8; c < n; c += 64 * 8) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(s + c);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    float v[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = clamp448(bf16_bits_to_f32(w[q] & 0xffff) * r);
-      v[2 * q + 1] = clamp448(bf16_bits_to_f32(w[q] >> 16) * r);
+    for (int i = 0; i < R; ++i) amax = chunk_amax(raw[i], amax);
+    amax = wave_max(amax);
+    scale = amax / 448.f;
+    r = amax > 0.f ? 448.f / amax : 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int c = (i * 64 + lane) * 8;
+      if (c < n) *reinterpret_cast<uint2*>(d + c) = amax > 0.f ? e4m3x8_scaled(raw[i], r) : make_uint2(0u, 0u);
     }
-    uint2 out;
-    out.x = amax > 0.f ? e4m3x4(v[0], v[1], v[2], v[3]) : 0u;
-    out.y = amax > 0.f ? e4m3x4(v[4], v[5], v[6], v[7]) : 0u;
-    *reinterpret_cast<uint2*>(d + c) = out;
+  } else {
+    for (int c = lane * 8; c < n; c += 64 * 8) amax = chunk_amax(*reinterpret_cast<const uint4*>(s + c), amax);
+    amax = wave_max(amax);
+    scale = amax / 448.f;
+    r = amax > 0.f ? 448.f / amax : 0.f;
+    for (int c = lane * 8; c < n; c += 64 * 8) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(s + c);
+      *reinterpret_cast<uint2*>(d + c) = amax > 0.f ? e4m3x8_scaled(raw, r) : make_uint2(0u, 0u);
+    }
   }
   if (lane == 0) *scale_out = scale;
 }

@@ -24,6 +24,7 @@ constexpr int QUANT_WAVES = 4;
 //   in place (h -> h8):    src = dst = inv_perm[p]
 //   plain (rows given):    src = dst = p  (inv_perm == null)
 // Pairs whose inv_perm entry is negative are skipped.  n % 8 == 0.
+template <int R>
 __global__ void __launch_bounds__(64 * QUANT_WAVES)
 quantize_rows_kernel(const uint16_t* __restrict__ src, int64_t ld_src, int n, int64_t pairs, int K, bool gather,
                      const int32_t* __restrict__ inv_perm, uint8_t* __restrict__ dst, int64_t ld_dst,
@@ -36,7 +37,7 @@ quantize_rows_kernel(const uint16_t* __restrict__ src, int64_t ld_src, int n, in
     if (drow < 0) return;
     srow = gather ? p / K : drow;
   }
-  wave_quantize_row_e4m3(src + srow * ld_src, n, dst + drow * ld_dst, scales + drow);
+  wave_quantize_row_e4m3<R>(src + srow * ld_src, n, dst + drow * ld_dst, scales + drow);
 }
 
 hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld_src, int n, int64_t pairs, int K, bool gather,
@@ -44,8 +45,14 @@ hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld_src, int n, int6
                                 hipStream_t st) {
   if (pairs == 0) return hipSuccess;
   const unsigned g = (unsigned)ceil_div(pairs, QUANT_WAVES);
-  quantize_rows_kernel<<<g, 64 * QUANT_WAVES, 0, st>>>(src, ld_src, n, pairs, K, gather, inv_perm, dst, ld_dst,
-                                                       scales);
+  // R 16-byte chunks per lane held in registers: the smallest instance that
+  // holds the whole row (rows of up to 512 R values are read once), so short
+  // rows keep the registers per wave low and many waves resident
+  auto kern = quantize_rows_kernel<16>;
+  if (n <= 64 * 8 * 2) kern = quantize_rows_kernel<2>;
+  else if (n <= 64 * 8 * 4) kern = quantize_rows_kernel<4>;
+  else if (n <= 64 * 8 * 8) kern = quantize_rows_kernel<8>;
+  kern<<<g, 64 * QUANT_WAVES, 0, st>>>(src, ld_src, n, pairs, K, gather, inv_perm, dst, ld_dst, scales);
   return hipGetLastError();
 }
 
