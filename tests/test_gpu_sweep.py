@@ -8,7 +8,7 @@ bias, raw or renormalised gates, a gate temperature, a skewing router
 offset) and sometimes a per-expert capacity, and runs the whole layer.  The
 oracle routes from the GPU's float32 scores (the scores themselves are
 checked against their rounding bound elsewhere), so expert indices --
-capacity decisions included -- must agree exactly, gates to 1e-5 and every
+capacity decisions included -- must agree exactly, gates to 1e-6 and every
 output row within the dtype tolerance."""
 import numpy as np
 import pytest
