@@ -15,6 +15,7 @@ usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --pmc-probe [--workload NAME] [--act-quant]   (under rocprofv3 --pmc)
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
        python bench.py --pmc-mfma-summary DIR [--workload NAME]
+       python bench.py --pmc-mem-summary L2_DIR L1_DIR [--workload NAME]
 """
 import argparse
 import hashlib
@@ -55,6 +56,8 @@ def parse():
                     help="with --pmc-probe: the fp8-activation (W8A8) products of the workload")
     ap.add_argument("--pmc-mfma-summary", metavar="DIR",
                     help="write profiles/mfma_*.md from a rocprofv3 --pmc pass over the MFMA counters")
+    ap.add_argument("--pmc-mem-summary", nargs=2, metavar=("L2_DIR", "L1_DIR"),
+                    help="write profiles/memory_path_*.md from the two memory-path counter passes")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_*.md from two rocprofv3 --pmc output directories")
     return ap.parse_args()
@@ -372,6 +375,86 @@ def pmc_mfma_summary(a):
                     f"{busy:.3f} x {ghz / 2.4:.3f} / {flops / alg:.3f} = {busy * ghz / 2.4 / (flops / alg):.3f} under "
                     "counter collection (the bench line's figure comes from uninstrumented launches, at a clock "
                     "that varies from box to box).\n\n")
+            f.write(f"- source_hash: {gemm_source_hash()}\n")
+        log(f"[bench] wrote {path}")
+
+
+MEM_COUNTERS_L2 = "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE"
+MEM_COUNTERS_L1 = "TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_PENDING_STALL_CYCLES_sum GRBM_GUI_ACTIVE"
+
+
+def pmc_mem_summary(a):
+    """Turn two rocprofv3 --pmc passes (MEM_COUNTERS_L2, then MEM_COUNTERS_L1;
+    csv output) into profiles/memory_path_<stage>_<workload>.md: per expert
+    GEMM, the L2 hit rate, the memory reads behind L2 (count, latency, how
+    many are in flight on average) and the L1 -> L2 read requests (latency
+    and the average in flight per CU, by Little's law: summed latency over
+    elapsed cycles)."""
+    import csv
+    import statistics
+
+    def read(d):
+        disp = {}
+        for root, _, files in os.walk(d):
+            for f in files:
+                if not f.endswith("counter_collection.csv"):
+                    continue
+                for r in csv.DictReader(open(os.path.join(root, f))):
+                    k = r["Kernel_Name"]
+                    if gemm_kernel_stage(k) is None:
+                        continue
+                    e = disp.setdefault(k, {}).setdefault(r["Dispatch_Id"], {
+                        "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                    e[r["Counter_Name"]] = float(r["Counter_Value"])
+        return disp
+
+    l2, l1 = read(a.pmc_mem_summary[0]), read(a.pmc_mem_summary[1])
+    cus, xccs = 256, 8
+    for k in l2:
+        if k not in l1 or len(l2[k]) < 3 or len(l1[k]) < 3:
+            continue
+        stage, a8 = gemm_kernel_stage(k)
+        cfg_name = a.workload + ("_w8a8" if a8 else "")
+        probe = " --act-quant" if a8 else ""
+        A, B = list(l2[k].values()), list(l1[k].values())
+        med = lambda ds, f: statistics.median(f(d) for d in ds)
+        cyc = lambda d: d["GRBM_GUI_ACTIVE"] / xccs
+        ms = med(A, lambda d: d["ns"]) / 1e6
+        ghz = med(A, lambda d: cyc(d) / d["ns"])
+        hit = med(A, lambda d: d["TCC_HIT_sum"] / (d["TCC_HIT_sum"] + d["TCC_MISS_sum"]))
+        rd = med(A, lambda d: d["TCC_EA0_RDREQ_sum"])
+        rd_lat = med(A, lambda d: d["TCC_EA0_RDREQ_LEVEL_sum"] / d["TCC_EA0_RDREQ_sum"])
+        rd_fly = med(A, lambda d: d["TCC_EA0_RDREQ_LEVEL_sum"] / cyc(d))
+        rd_rate = med(A, lambda d: d["TCC_EA0_RDREQ_sum"] * 128 / (d["ns"] * 1e-9) / 1e12)
+        q = med(B, lambda d: d["TCP_TCC_READ_REQ_sum"])
+        q_lat = med(B, lambda d: d["TCP_TCC_READ_REQ_LATENCY_sum"] / d["TCP_TCC_READ_REQ_sum"])
+        q_fly = med(B, lambda d: d["TCP_TCC_READ_REQ_LATENCY_sum"] / cyc(d) / cus)
+        pend = med(B, lambda d: d["TCP_PENDING_STALL_CYCLES_sum"] / cyc(d) / cus)
+        path = os.path.join(ROOT, "profiles", f"memory_path_{stage}_{cfg_name}.md")
+        with open(path, "w") as f:
+            f.write(f"# Memory path: `{stage}` GEMM, {cfg_name} workload\n\n")
+            f.write("Commands (one MI355X, repository root; two counter passes, then this summary):\n\n```\n")
+            f.write(f"rocprofv3 --pmc {MEM_COUNTERS_L2} -d gpurun_out/pmc_l2 -o a --output-format csv -- "
+                    f"python -u bench.py --pmc-probe --workload {a.workload}{probe}\n")
+            f.write(f"rocprofv3 --pmc {MEM_COUNTERS_L1} -d gpurun_out/pmc_l1 -o b --output-format csv -- "
+                    f"python -u bench.py --pmc-probe --workload {a.workload}{probe}\n")
+            f.write(f"python bench.py --workload {a.workload} --pmc-mem-summary gpurun_out/pmc_l2 gpurun_out/pmc_l1\n"
+                    "```\n\n")
+            f.write(f"Kernel: `{k}` ({len(A)} dispatches, medians).  Cycles = GRBM_GUI_ACTIVE / {xccs} "
+                    f"(summed over the XCCs); {cus} CUs.\n\n")
+            f.write("| quantity | value |\n|:--|--:|\n")
+            f.write(f"| dispatch duration under counter collection | {ms:.3f} ms |\n")
+            f.write(f"| shader clock | {ghz:.2f} GHz |\n")
+            f.write(f"| L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS) | {100 * hit:.1f} % |\n")
+            f.write(f"| memory reads behind L2: TCC_EA0_RDREQ | {rd:.4g} |\n")
+            f.write(f"| their rate at 128 B each | {rd_rate:.2f} TB/s |\n")
+            f.write(f"| memory read latency: TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ | {rd_lat:.0f} cycles |\n")
+            f.write(f"| memory reads in flight on average: TCC_EA0_RDREQ_LEVEL / cycles | {rd_fly:.0f} |\n")
+            f.write(f"| L1 -> L2 read requests: TCP_TCC_READ_REQ | {q:.4g} |\n")
+            f.write(f"| L1 -> L2 read latency: TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ | {q_lat:.0f} cycles |\n")
+            f.write(f"| L1 -> L2 reads in flight per CU: TCP_TCC_READ_REQ_LATENCY / cycles / {cus} | {q_fly:.1f} |\n")
+            f.write(f"| L1 cycles stalled on pending L2 reads: TCP_PENDING_STALL_CYCLES / cycles / {cus} | "
+                    f"{100 * pend:.0f} % |\n\n")
             f.write(f"- source_hash: {gemm_source_hash()}\n")
         log(f"[bench] wrote {path}")
 
@@ -747,6 +830,9 @@ def main():
         return
     if a.pmc_mfma_summary:
         pmc_mfma_summary(a)
+        return
+    if a.pmc_mem_summary:
+        pmc_mem_summary(a)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
