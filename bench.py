@@ -16,6 +16,7 @@ usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
        python bench.py --pmc-mfma-summary DIR [--workload NAME]
        python bench.py --pmc-mem-summary L2_DIR L1_DIR [--workload NAME]
+       python bench.py --trace-table KERNELS_SUMMARY_MD   (rocpd2summary markdown -> this library's rows)
 """
 import argparse
 import hashlib
@@ -56,6 +57,8 @@ def parse():
                     help="with --pmc-probe: the fp8-activation (W8A8) products of the workload")
     ap.add_argument("--pmc-mfma-summary", metavar="DIR",
                     help="write profiles/mfma_*.md from a rocprofv3 --pmc pass over the MFMA counters")
+    ap.add_argument("--trace-table", metavar="KERNELS_SUMMARY_MD",
+                    help="print the rows of this library's kernels from a rocpd2summary kernel table")
     ap.add_argument("--pmc-mem-summary", nargs=2, metavar=("L2_DIR", "L1_DIR"),
                     help="write profiles/memory_path_*.md from the two memory-path counter passes")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -377,6 +380,25 @@ def pmc_mfma_summary(a):
                     "that varies from box to box).\n\n")
             f.write(f"- source_hash: {gemm_source_hash()}\n")
         log(f"[bench] wrote {path}")
+
+
+def trace_table(path):
+    """The library's kernels (namespace sfl) from a rocpd2summary markdown
+    kernel table (durations in ns), as a markdown table in microseconds,
+    longest total time first."""
+    import re
+    rows = []
+    for line in open(path):
+        if "sfl::" not in line:
+            continue
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        name = re.sub(r"\(.*$", "", re.sub(r"^void ", "", cells[0]))
+        rows.append((float(cells[2]), name, int(cells[1]), float(cells[3]) / 1e3, float(cells[5]) / 1e3,
+                     float(cells[6]) / 1e3))
+    rows.sort(reverse=True)
+    print("| kernel | calls | avg (us) | min (us) | max (us) |\n|:--|--:|--:|--:|--:|")
+    for _, n, c, avg, mn, mx in rows:
+        print(f"| `{n}` | {c} | {avg:.1f} | {mn:.1f} | {mx:.1f} |")
 
 
 MEM_COUNTERS_L2 = "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE"
@@ -833,6 +855,9 @@ def main():
         return
     if a.pmc_mem_summary:
         pmc_mem_summary(a)
+        return
+    if a.trace_table:
+        trace_table(a.trace_table)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
