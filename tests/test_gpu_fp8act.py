@@ -26,8 +26,12 @@ def _bf16(a):
     return t.to(DEV), t.float().numpy()
 
 
+# Row lengths on both sides of each register-block size of the quantiser
+# (1024, 2048, 4096 and 8192 values held in registers; longer rows are read
+# twice): 8-136 and 1024, 1032-2048, 4096, 7168-8192, then 8200 and 14336.
 @pytest.mark.parametrize("rows,n,seed", [(1, 8, 0), (37, 64, 1), (300, 2048, 2), (64, 7168, 3), (16, 14336, 4),
-                                         (1000, 136, 5)])
+                                         (1000, 136, 5), (12, 1024, 6), (9, 1032, 7), (40, 4096, 8),
+                                         (5, 8192, 9), (3, 8200, 10)])
 def test_quantize_rows_bit_exact(rows, n, seed):
     rng = np.random.default_rng(seed)
     v = rng.standard_normal((rows, n)) * np.exp(rng.uniform(-20, 20, (rows, 1)))

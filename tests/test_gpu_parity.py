@@ -131,6 +131,31 @@ def test_fused_router_both_row_splits(S, d, E, act):
     np.testing.assert_allclose(gate.cpu().numpy(), O.gate_weights(got, o_idx, 1), rtol=0, atol=GATE_TOL)
 
 
+@pytest.mark.parametrize("S,E", [(1000, 64), (16390, 64), (33001, 64), (8300, 256)])
+def test_router_gemm_row_tiles(S, E):
+    """The MFMA router product (bf16, E % 64 == 0) takes the largest row tile
+    of 128, 64 or 32 that still gives every compute unit a tile: batches that
+    take each of the three on 256 compute units (S = 33001 and 8300 with 128
+    rows, 16390 with 64, 1000 with 32), the last tile partly past the batch.
+    Scores within the rounding bound of the oracle's, and the selection and
+    gates exact given those scores."""
+    cfg = D.MoEConfig("rg", S=S, d=320, d_ff=64, E=E, K=2, router_offset="normal", offset_beta=0.5, seed=5)
+    print(f"router GEMM S={S} E={E}", flush=True)
+    x, wr = D.tokens(cfg, DEV), D.router_weight(cfg, DEV)
+    rb = D.router_bias(cfg)
+    p = problem(cfg)
+    lo = torch.empty((S, E), dtype=torch.float32, device=DEV)
+    idx, gate = M.moe_route(p, x, wr, rb.to(DEV), None, logits_out=lo)
+    sync()
+    ov = {"x": raw(x), "W_r": raw(wr), "router_bias": rb.numpy(), "select_bias": None}
+    ref = oracle_logits(cfg, ov).astype(np.float64)
+    got = lo.cpu().numpy()
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= logit_bound(cfg, ov, ref) + 1e-30)
+    o_idx = O.select_experts(got, cfg.K)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    np.testing.assert_allclose(gate.cpu().numpy(), O.gate_weights(got, o_idx, 1), rtol=0, atol=GATE_TOL)
+
+
 # ------------------------------------------------------------------ permute
 def _permute_case(E, K, idx, d=64, act="bf16"):
     S = idx.shape[0]
