@@ -25,6 +25,12 @@
 namespace sfl {
 
 constexpr int ROUTER_WAVES = 4;  // waves of a router block
+// Large batches with a small router matrix: blocks of 16 waves (one token
+// each) stage W_r in LDS once instead of every wave reading all of it through
+// its L1 (64 KB per token at the Mixtral shape).
+constexpr int ROUTER_LDS_WAVES = 16;
+constexpr int ROUTER_LDS_BYTES = 64 * 1024;
+constexpr int ROUTER_LDS_SPANS = 8;   // the row's 16-byte-per-lane spans held in registers
 
 // Select K experts from this token's logits and write indices and gates.
 // lg[r]: unbiased logit of expert r*64 + lane (-inf where that is >= E).
@@ -77,28 +83,85 @@ __device__ __forceinline__ void select_and_gate(const float (&lg)[R], int E, int
 // the token's first wave then selects.  Splitting a row over several waves
 // shortens the chain of dependent loads each wave waits on, which is what a
 // small batch pays for; a large batch has waves enough to hide it (WPT = 1).
-template <typename T, int EC, int R, int WPT>
-__global__ void __launch_bounds__(64 * ROUTER_WAVES)
+// WR_LDS (WPT = 1, E d sizeof(T) <= ROUTER_LDS_BYTES, d <= ROUTER_LDS_SPANS
+// spans): the block first copies W_r to LDS and the waves read it there;
+// every lane sums the same products in the same order as when it reads W_r
+// from memory, so the scores are the same bits.
+template <typename T, int EC, int R, int WPT, int WAVES = ROUTER_WAVES, bool WR_LDS = false>
+__global__ void __launch_bounds__(64 * WAVES)
 router_fused_kernel(int64_t S, int d, int E, int K, const T* __restrict__ x,
                     const T* __restrict__ Wr, const float* __restrict__ rbias,
                     const float* __restrict__ sbias, int n_groups, int topk_groups, int renorm,
                     float inv_tau, float* __restrict__ logits_out, int32_t* __restrict__ idx,
                     float* __restrict__ gate) {
-  static_assert(ROUTER_WAVES % WPT == 0, "whole tokens per block");
-  __shared__ float part[ROUTER_WAVES][64 * R];
+  static_assert(WAVES % WPT == 0, "whole tokens per block");
+  static_assert(!WR_LDS || WPT == 1, "W_r in LDS: one wave per token");
+  __shared__ float part[WAVES][64 * R];
+  __shared__ uint4 wr_s[WR_LDS ? ROUTER_LDS_BYTES / 16 : 1];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = wave % WPT;  // this wave's share of the token's row
-  const int64_t t = (int64_t)blockIdx.x * (ROUTER_WAVES / WPT) + wave / WPT;
+  const int64_t t = (int64_t)blockIdx.x * (WAVES / WPT) + wave / WPT;
   const bool live = t < S;     // every wave still reaches the barrier
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
   constexpr int SPAN = 64 * VEC;
   const T* xr = x + (live ? t : 0) * d;
+  // WR_LDS: the lane's chunks of the token's row are loaded first, all at
+  // once (d <= ROUTER_LDS_SPANS spans, checked by the host), and stay in
+  // registers while W_r is copied
+  uint4 xrow[WR_LDS ? ROUTER_LDS_SPANS : 1];
+  if constexpr (WR_LDS) {
+#pragma unroll
+    for (int k = 0; k < ROUTER_LDS_SPANS; ++k) {
+      const int i0 = k * SPAN + lane * VEC;
+      xrow[k] = (live && i0 < d) ? *reinterpret_cast<const uint4*>(xr + i0) : make_uint4(0, 0, 0, 0);
+    }
+    const int chunks = E * d / VEC;  // the host checked E d sizeof(T) <= ROUTER_LDS_BYTES
+    for (int c = threadIdx.x; c < chunks; c += 64 * WAVES) wr_s[c] = reinterpret_cast<const uint4*>(Wr)[c];
+    __syncthreads();
+  }
 
   for (int e0 = 0; e0 < E && live; e0 += EC) {
     float acc[EC];
 #pragma unroll
     for (int j = 0; j < EC; ++j) acc[j] = 0.f;
+    if constexpr (WR_LDS) {
+      // spans in the same order as the loop below (WPT = 1)
+#pragma unroll
+      for (int k = 0; k < ROUTER_LDS_SPANS; ++k) {
+        if (k * SPAN >= d) break;
+        const int i0 = k * SPAN + lane * VEC;
+        if (i0 >= d) continue;
+        float xv[VEC];
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t w[4] = {xrow[k].x, xrow[k].y, xrow[k].z, xrow[k].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { xv[2 * q] = bf16_bits_to_f32(w[q] & 0xffff); xv[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16); }
+        } else {
+          xv[0] = __uint_as_float(xrow[k].x); xv[1] = __uint_as_float(xrow[k].y);
+          xv[2] = __uint_as_float(xrow[k].z); xv[3] = __uint_as_float(xrow[k].w);
+        }
+#pragma unroll
+        for (int j = 0; j < EC; ++j) {
+          if (e0 + j < E) {
+            const uint4 raw = wr_s[((e0 + j) * d + i0) / VEC];
+            float s = acc[j];
+            if constexpr (sizeof(T) == 2) {
+              const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                s = fmaf(xv[2 * q], bf16_bits_to_f32(w[q] & 0xffff), s);
+                s = fmaf(xv[2 * q + 1], bf16_bits_to_f32(w[q] >> 16), s);
+              }
+            } else {
+              s = fmaf(xv[0], __uint_as_float(raw.x), s); s = fmaf(xv[1], __uint_as_float(raw.y), s);
+              s = fmaf(xv[2], __uint_as_float(raw.z), s); s = fmaf(xv[3], __uint_as_float(raw.w), s);
+            }
+            acc[j] = s;
+          }
+        }
+      }
+    } else
 #pragma unroll 2
     for (int s0 = sub * SPAN; s0 < d; s0 += WPT * SPAN) {
       const int i0 = s0 + lane * VEC;
@@ -311,10 +374,18 @@ static hipError_t launch_fused_T(const Problem& p, const void* x, const void* Wr
   const int R = (p.E + 63) / 64;
   // a row per wave once the batch alone fills the chip with waves
   const bool split = p.S < 2048;
+  // ... and then W_r in LDS when it fits
+  const bool wr_lds = !split && (int64_t)p.E * p.d * (int64_t)sizeof(T) <= ROUTER_LDS_BYTES &&
+                      p.d <= ROUTER_LDS_SPANS * 64 * (16 / (int)sizeof(T));
   const dim3 grid((unsigned)(split ? p.S : ceil_div(p.S, ROUTER_WAVES))), block(64 * ROUTER_WAVES);
+  const dim3 grid_lds((unsigned)ceil_div(p.S, ROUTER_LDS_WAVES)), block_lds(64 * ROUTER_LDS_WAVES);
 #define SFL_FUSED(RR)                                                                              \
   do {                                                                                             \
-    if (split)                                                                                     \
+    if (wr_lds)                                                                                    \
+      router_fused_kernel<T, EC, RR, 1, ROUTER_LDS_WAVES, true><<<grid_lds, block_lds, 0, st>>>(   \
+          p.S, p.d, p.E, p.K, (const T*)x, (const T*)Wr, rb, sb, p.n_groups, p.topk_groups,        \
+          p.renormalize, p.inv_tau, lo, idx, gate);                                                \
+    else if (split)                                                                                \
       router_fused_kernel<T, EC, RR, ROUTER_WAVES><<<grid, block, 0, st>>>(                        \
           p.S, p.d, p.E, p.K, (const T*)x, (const T*)Wr, rb, sb, p.n_groups, p.topk_groups,        \
           p.renormalize, p.inv_tau, lo, idx, gate);                                                \
