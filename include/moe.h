@@ -98,8 +98,9 @@ typedef enum {
  *    moe_quantize_rows does, and both products run on fp8 MFMAs; the result
  *    is dequantised by row scale times weight channel scale.  Needs
  *    act_dtype BF16, w_dtype FP8_E4M3, d and d_ff multiples of 128 (else
- *    MOE_ERR_UNSUPPORTED).  moe_permute and the expert entry points take
- *    bf16 activations and return MOE_ERR_UNSUPPORTED when it is set.
+ *    MOE_ERR_UNSUPPORTED).  moe_permute, moe_expert_ffn, moe_expert_up and
+ *    moe_expert_down (bf16 activations) return MOE_ERR_UNSUPPORTED when it
+ *    is set; moe_expert_up_a8 and moe_expert_down_a8 require it.
  *    0 = activations in act_dtype; other values: MOE_ERR_INVALID_ARG.
  *  - Limits: 1 <= E <= 512, 1 <= K <= min(E, 64), d and d_ff multiples of 64,
  *    S < 2^24 and S * K < 2^26 (every kernel launch stays below 2^32
@@ -216,9 +217,11 @@ int32_t moe_expert_down(const moe_problem* p, const void* h, const int32_t* expe
  *   moe_expert_down_a8: y_perm[r] = dq(h8[r]) W2_e + b2_e             (bf16)
  * where dq(codes[r]) = decode(codes[r]) * scale[r]: e4m3 rows with one
  * float32 scale per row, as moe_quantize_rows writes them (the layer with
- * act_quant = 1 runs exactly moe_permute's gather, moe_quantize_rows of the
- * gathered rows, moe_expert_up_a8, moe_quantize_rows of h,
- * moe_expert_down_a8).  Both operands go to the fp8 MFMAs; the float32 sum
+ * act_quant = 1 computes exactly what moe_permute's gather (for the same
+ * problem with act_quant = 0), moe_quantize_rows of the gathered rows,
+ * moe_expert_up_a8, moe_quantize_rows of h and moe_expert_down_a8 compute;
+ * it quantises each token's row once and the up product reads those codes
+ * in place).  Both operands go to the fp8 MFMAs; the float32 sum
  * is multiplied by row scale x channel scale in the epilogue.
  *   x8 [rows_capacity][d], h8 [rows_capacity][d_ff]: uint8 codes;
  *   x_scale, h_scale [rows_capacity] float32; w1_scale / w2_scale required.

@@ -135,6 +135,38 @@ def test_layer_w8a8_dsv3_full_size():
     assert float((a - b).abs().max()) <= TOL["fp8"] * float(b.abs().max())
 
 
+@pytest.mark.parametrize("S,E,K,seed", [(2048, 8, 2, 0), (640, 16, 2, 1), (24, 8, 2, 2)])
+def test_layer_w8a8_equals_its_stages(S, E, K, seed):
+    """The W8A8 layer quantises each token's row once and its up product
+    reads those codes in place; the stage entry points gather x per (token,
+    slot) pair and quantise the gathered rows.  Both compute the same codes
+    and the same products, so the outputs agree bit for bit (prefill, mid
+    and decode tiles)."""
+    base = D.CONFIGS["dsv3_fp8"]
+    cfg = dataclasses.replace(base, name=f"w8a8_st_{S}", S=S, d=512, d_ff=768, E=E, K=K, n_groups=1,
+                              topk_groups=1, select_bias_var=0.0, router_offset="normal", offset_beta=0.5, seed=seed)
+    inp = D.make_inputs(cfg, device=DEV)
+    p = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                       cfg.renormalize, 1.0, 0, 1)
+    # routing, dispatch and combine of the stage path on the same problem
+    # with bf16 activations (moe_permute refuses act_quant = 1)
+    p0 = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
+                        cfg.renormalize)
+    assert M.moe_tile_m(p0) == M.moe_tile_m(p)
+    y = M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                            inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"])
+    idx, gate = M.moe_route(p0, inp["x"], inp["W_r"], inp["router_bias"], inp["select_bias"])
+    counts, offsets, perm, inv, x_perm = M.moe_permute(p0, idx, inp["x"])
+    x8, xs = M.moe_quantize_rows(x_perm)
+    h = M.moe_expert_up_a8(p, x8, xs, counts, offsets, inp["W1"], inp["b1"], inp["w1_scale"])
+    h8, hs = M.moe_quantize_rows(h)
+    y_perm = M.moe_expert_down_a8(p, h8, hs, counts, offsets, inp["W2"], inp["b2"], inp["w2_scale"])
+    y2 = M.moe_combine(p0, y_perm, inv, gate)
+    sync()
+    print(f"w8a8 layer vs stages S={S}: regime tile {M.moe_tile_m(p)}", flush=True)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 def test_layer_w8a8_deterministic():
     cfg = D.CONFIGS["dsv3_fp8"]
     inp = gpu_inputs("dsv3_fp8")
