@@ -429,6 +429,41 @@ def test_empty_batch_noop():
     assert torch.all(y == 7.0)
 
 
+LAYER_VS_STAGES = [
+    ("decode", None),                                                           # 16-row tiles, rows in place
+    ("dsv3_fp8", None),                                                         # 128-row fp8 tiles, in place
+    ("mixtral_prefill", None),                                                  # four-wave kernel, gathered rows
+    ("mid_bf16", dict(S=600, d=512, d_ff=768, E=8, K=2)),                       # 128-row bf16 tiles, in place
+    ("prefill_n128", dict(S=2048, d=512, d_ff=640, E=8, K=2)),                  # 256 x 128 tiles, in place
+]
+
+
+@pytest.mark.parametrize("name,kw", LAYER_VS_STAGES, ids=[n for n, _ in LAYER_VS_STAGES])
+def test_layer_equals_its_stages(name, kw):
+    """moe_layer_forward against moe_route, moe_permute (gathered rows),
+    moe_expert_up / moe_expert_down and moe_combine on the same problem: the
+    layer's up product reads the token rows in place where its tiles allow,
+    the stage path reads the gathered copy, and the outputs agree bit for
+    bit."""
+    if kw is None:
+        cfg = D.CONFIGS[name]
+        inp = gpu_inputs(name)
+    else:
+        cfg = D.MoEConfig(name, router_offset="normal", offset_beta=0.5, seed=3, **kw)
+        inp = D.make_inputs(cfg, device=DEV)
+    p = problem(cfg)
+    print(f"layer vs stages {name}: tile {M.moe_tile_m(p)}", flush=True)
+    y = M.moe_layer_forward(p, inp["x"], inp["W_r"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                            inp["router_bias"], inp["select_bias"], inp["w1_scale"], inp["w2_scale"])
+    idx, gate = M.moe_route(p, inp["x"], inp["W_r"], inp["router_bias"], inp["select_bias"])
+    counts, offsets, perm, inv, x_perm = M.moe_permute(p, idx, inp["x"])
+    h, y_perm = M.moe_expert_ffn(p, x_perm, counts, offsets, inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                                 inp["w1_scale"], inp["w2_scale"])
+    y2 = M.moe_combine(p, y_perm, inv, gate)
+    sync()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 @pytest.mark.parametrize("name", ["zipf_skew", "decode"])
 def test_deterministic(name):
     cfg = D.CONFIGS[name]
