@@ -229,8 +229,9 @@ int32_t oracle_layer_forward(const double* x, const double* w_r, const float* ro
       for (int32_t c = 0; c < d; ++c) y[t * d + c] += gate[t * K + k] * o[c];
     }
   }
-  if (topk_idx_out) std::memcpy(topk_idx_out, idx.data(), idx.size() * sizeof(int32_t));
-  if (topk_gate_out) std::memcpy(topk_gate_out, gate.data(), gate.size() * sizeof(double));
+  // (no tokens: the vectors own no storage and there is nothing to copy)
+  if (topk_idx_out && !idx.empty()) std::memcpy(topk_idx_out, idx.data(), idx.size() * sizeof(int32_t));
+  if (topk_gate_out && !gate.empty()) std::memcpy(topk_gate_out, gate.data(), gate.size() * sizeof(double));
   return 0;
 }
 
