@@ -286,7 +286,10 @@ int32_t moe_load_stats(const moe_problem* p, const int32_t* expert_counts, const
  *     scales[r] = amax / 448,   codes[r][i] = e4m3(clamp(v * (448 / amax),
  *     -448, 448)), round to nearest even (OCP E4M3FN codes),
  * each quotient and product one float32 operation; the row's value is
- * decode(code) * scale.  A row of zeros gets scale 0 and codes 0.
+ * decode(code) * scale.  A row of zeros gets scale 0 and codes 0.  Where
+ * 448 / amax overflows float32 (amax below about 1.3e-36) the row and amax
+ * are first multiplied by 2^64 (exact): codes = e4m3(clamp((v * 2^64) *
+ * (448 / (amax * 2^64)))), what an unbounded exponent range would give.
  *   codes [rows][n] uint8 and scales [rows] float32 are written.
  *   n: a positive multiple of 8; rows >= 0 (0 is a no-op), < 2^26 (else
  *   MOE_ERR_UNSUPPORTED).

@@ -121,7 +121,11 @@ def quantize_rows_e4m3(v: np.ndarray):
     largest |v|, the scale is s = amax / 448 and the codes are q =
     encode(clip(v * r, -448, 448)) with r = 448 / amax (each quotient and
     the product one float32 operation); the row's value is decode(q) * s.
-    A row of zeros gets s = 0 and codes 0.
+    A row of zeros gets s = 0 and codes 0.  When 448 / amax overflows
+    float32 (amax below about 1.3e-36, which bf16 rows can reach) the row and amax are first multiplied by 2^64 (exact), so that
+    r = 448 / (amax 2^64) and t = (v 2^64) r: the codes the same steps give
+    with an unbounded exponent range (reading: the pages fix the per-row
+    scale, not float32's overflow).
     FP8 E4M3 is the format the pages recommend for expert weights ([P1]
     section 3.3); applying it to the activations with a per-row (per-token)
     scale is the W8A8 reading, so that both GEMM operands are fp8.
@@ -130,8 +134,12 @@ def quantize_rows_e4m3(v: np.ndarray):
     amax = np.abs(v).max(axis=1) if v.shape[1] else np.zeros(v.shape[0], np.float32)
     amax = amax.astype(np.float32)
     s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    r = (np.float32(E4M3_MAX) / np.where(amax > 0, amax, np.float32(1.0))).astype(np.float32)
-    t = (v * r[:, None]).astype(np.float32)
+    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        tiny = np.isinf((np.float32(E4M3_MAX) / safe).astype(np.float32))   # 448 / amax overflows
+    pre = np.where(tiny, np.float32(2.0 ** 64), np.float32(1.0)).astype(np.float32)
+    r = (np.float32(E4M3_MAX) / (safe * pre).astype(np.float32)).astype(np.float32)
+    t = ((v * pre[:, None]).astype(np.float32) * r[:, None]).astype(np.float32)
     t = np.clip(t, np.float32(-E4M3_MAX), np.float32(E4M3_MAX)).astype(np.float32)
     codes = encode_e4m3fn(t)
     codes[s == 0] = 0

@@ -98,14 +98,15 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 }
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
-// Eight bf16 values (one 16-byte chunk) times r, clamped, as e4m3 codes.
-__device__ __forceinline__ uint2 e4m3x8_scaled(uint4 raw, float r) {
+// Eight bf16 values (one 16-byte chunk) times pre, then times r, clamped,
+// as e4m3 codes.  pre is 1 or 2^64 (exact either way).
+__device__ __forceinline__ uint2 e4m3x8_scaled(uint4 raw, float pre, float r) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   float v[8];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    v[2 * q] = clamp448(bf16_bits_to_f32(w[q] & 0xffff) * r);
-    v[2 * q + 1] = clamp448(bf16_bits_to_f32(w[q] >> 16) * r);
+    v[2 * q] = clamp448((bf16_bits_to_f32(w[q] & 0xffff) * pre) * r);
+    v[2 * q + 1] = clamp448((bf16_bits_to_f32(w[q] >> 16) * pre) * r);
   }
   return make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7]));
 }
@@ -119,11 +120,25 @@ __device__ __forceinline__ float chunk_amax(uint4 raw, float amax) {
   return amax;
 }
 
+// r = 448 / amax, or 448 / (amax 2^64) with pre = 2^64 where the first
+// quotient overflows; amax = 0 gives r = 0.
+__device__ __forceinline__ float row_factor(float amax, float& pre) {
+  pre = 1.f;
+  if (!(amax > 0.f)) return 0.f;
+  const float r = 448.f / amax;
+  if (!__builtin_isinf(r)) return r;
+  pre = 0x1p64f;
+  return 448.f / (amax * pre);
+}
+
 // One row of n bf16 values (n % 8 == 0) -> e4m3 codes and one float32 scale,
 // by the whole wave:  amax = max |v|,  scale = amax / 448,  r = 448 / amax,
 // code = e4m3(clamp(v * r, -448, 448)); a row of zeros gets scale 0 and
 // codes 0.  Each quotient and product is one float32 operation, so the codes
-// are a function of the bf16 inputs alone.  Rows of up to 512 R values are
+// are a function of the bf16 inputs alone.  When 448 / amax overflows
+// float32 (amax below about 1.3e-36) the row and amax are first multiplied
+// by 2^64, exactly: r = 448 / (amax 2^64), code = e4m3(clamp((v 2^64) r)),
+// the codes an unbounded exponent range would give.  Rows of up to 512 R values are
 // read once, all of a lane's chunks in flight together, and held in
 // registers for the second step; longer rows are read twice (the second
 // time from cache).
@@ -131,7 +146,7 @@ template <int R>
 __device__ __forceinline__ void wave_quantize_row_e4m3(const uint16_t* __restrict__ s, int n,
                                                        uint8_t* __restrict__ d, float* __restrict__ scale_out) {
   const int lane = lane_id();
-  float amax = 0.f, scale, r;
+  float amax = 0.f, scale, r, pre;
   if (n <= 64 * 8 * R) {
     uint4 raw[R];
 #pragma unroll
@@ -143,20 +158,20 @@ __device__ __forceinline__ void wave_quantize_row_e4m3(const uint16_t* __restric
     for (int i = 0; i < R; ++i) amax = chunk_amax(raw[i], amax);
     amax = wave_max(amax);
     scale = amax / 448.f;
-    r = amax > 0.f ? 448.f / amax : 0.f;
+    r = row_factor(amax, pre);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int c = (i * 64 + lane) * 8;
-      if (c < n) *reinterpret_cast<uint2*>(d + c) = amax > 0.f ? e4m3x8_scaled(raw[i], r) : make_uint2(0u, 0u);
+      if (c < n) *reinterpret_cast<uint2*>(d + c) = amax > 0.f ? e4m3x8_scaled(raw[i], pre, r) : make_uint2(0u, 0u);
     }
   } else {
     for (int c = lane * 8; c < n; c += 64 * 8) amax = chunk_amax(*reinterpret_cast<const uint4*>(s + c), amax);
     amax = wave_max(amax);
     scale = amax / 448.f;
-    r = amax > 0.f ? 448.f / amax : 0.f;
+    r = row_factor(amax, pre);
     for (int c = lane * 8; c < n; c += 64 * 8) {
       const uint4 raw = *reinterpret_cast<const uint4*>(s + c);
-      *reinterpret_cast<uint2*>(d + c) = amax > 0.f ? e4m3x8_scaled(raw, r) : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(d + c) = amax > 0.f ? e4m3x8_scaled(raw, pre, r) : make_uint2(0u, 0u);
     }
   }
   if (lane == 0) *scale_out = scale;

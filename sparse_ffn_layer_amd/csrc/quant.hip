@@ -9,7 +9,10 @@
 //   code = e4m3(clamp(v * r, -448, 448))  (round to nearest even),
 // and the row's value is decode(code) * s; a row of zeros gets s = 0 and
 // codes 0.  Each quotient and product is one float32 operation, so the codes
-// are a function of the bf16 inputs alone.
+// are a function of the bf16 inputs alone.  Where 448 / amax overflows
+// float32 (amax below about 1.3e-36) the row and amax are first multiplied
+// by 2^64, which is exact, so such rows get the codes an unbounded exponent
+// range would give.
 //
 // One wave per row (wave_quantize_row_e4m3 in common.h).
 #include "common.h"

@@ -75,6 +75,27 @@ def test_quantize_rows_ties_and_subnormals():
     np.testing.assert_array_equal(scales.cpu().numpy(), o_scales)
 
 
+def test_quantize_rows_tiny_rows():
+    """Rows whose 448 / amax overflows float32 (amax below about 1.3e-36,
+    down to bf16 subnormals) against the oracle, codes and scales bit for
+    bit: both scale such rows up by 2^64 first."""
+    rng = np.random.default_rng(21)
+    rows, n = 48, 264
+    v = rng.standard_normal((rows, n)) * np.exp2(-rng.integers(112, 142, (rows, 1)).astype(np.float64))
+    v[0] = 0.0
+    v[1, :] = 2.0 ** -133 * np.arange(n)                    # bf16 subnormals and a zero
+    v[2, ::2] = 0.0
+    src, vals = _bf16(v)
+    amax = np.abs(vals).max(axis=1)
+    with np.errstate(divide="ignore", over="ignore"):
+        assert np.sum(np.isinf(np.float32(448) / amax[1:])) >= 20   # most rows take the scaled-up path
+    codes, scales = M.moe_quantize_rows(src)
+    sync()
+    o_codes, o_scales = O.quantize_rows_e4m3(vals)
+    np.testing.assert_array_equal(scales.cpu().numpy(), o_scales)
+    np.testing.assert_array_equal(codes.cpu().numpy(), o_codes)
+
+
 def _layer_w8a8(cfg, inp, tokens, cap=0):
     p = M.make_problem(cfg.S, cfg.d, cfg.d_ff, cfg.E, cfg.K, cfg.act, cfg.w, cfg.n_groups, cfg.topk_groups,
                        cfg.renormalize, 1.0, cap, 1)

@@ -77,6 +77,34 @@ def test_quantize_rows_closed_forms():
     np.testing.assert_array_equal(s2, (s * np.float32(32)).astype(np.float32))
 
 
+def test_quantize_rows_tiny_rows_are_power_of_two_copies():
+    """Rows whose 448 / amax overflows float32 (amax below about 1.3e-36)
+    get the codes of the same row scaled up by a power of two, and the
+    scale amax / 448 (subnormal here) as one float32 quotient.  Elements
+    are bf16 values (8 significant bits) in [2^-8, 1], so every scaled value
+    down to 2^-133 is still exact in float32 (subnormal spacing 2^-149)."""
+    rng = np.random.default_rng(11)
+    v = (np.sign(rng.standard_normal((6, 40))) * np.exp2(rng.uniform(-8, 0, (6, 40)))).astype(np.float32)
+    v = (v.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)   # truncate to bf16 values
+    v[:, 0] = 1.0                                  # amax = 1 in every row
+    q, _ = O.quantize_rows_e4m3(v)
+    for k in (118, 119, 120, 125):                 # 448 * 2^119 < FLT_MAX < 448 * 2^120
+        vs = (v * np.float32(2.0 ** -k)).astype(np.float32)
+        assert np.all(vs.astype(np.float64) == v.astype(np.float64) * 2.0 ** -k)
+        with np.errstate(over="ignore"):
+            assert np.isinf(np.float32(448) / np.float32(2.0 ** -k)) == (k >= 120)
+        qs, ss = O.quantize_rows_e4m3(vs)
+        np.testing.assert_array_equal(qs, q)
+        np.testing.assert_array_equal(ss, np.full(6, np.float32(2.0 ** -k) / np.float32(448), np.float32))
+    # float32 subnormal inputs: the largest lands on 448 (0x7E), half of it
+    # on -224 (0xF6), a zero stays 0, and 3/32 of it, 42, is the tie
+    # between 40 (0x62) and 44 (0x63) that goes to the even code
+    sub = np.array([[2.0 ** -140, -(2.0 ** -141), 0.0, 3 * 2.0 ** -145]], np.float32)
+    qs, ss = O.quantize_rows_e4m3(sub)
+    np.testing.assert_array_equal(qs[0], [0x7E, 0xF6, 0x00, 0x62])
+    assert ss[0] == np.float32(np.float32(2.0 ** -140) / np.float32(448))
+
+
 def test_quantize_rows_against_torch_conversion():
     rng = np.random.default_rng(5)
     v = rng.standard_normal((20, 64)).astype(np.float32)
