@@ -40,29 +40,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
-// GeLU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), the erf form.  erf is
+// GeLU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), the erf form, written
+// as  max(x, 0) - |x|/2 * erfc(|x| / sqrt 2)  (the same function; the small
+// term is a product, so negative x loses nothing to cancellation).  erfc is
 // evaluated with Abramowitz & Stegun, Handbook of Mathematical Functions,
-// formula 7.1.26 (|error| <= 1.5e-7 for x >= 0, odd symmetry for x < 0):
-//   erf(z) ~ 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2),
-//   t = 1 / (1 + p z).
-// About 15 VALU operations (two of them transcendental) per value, less than
-// half of a general-purpose erff; the error is far below the rounding of the
-// bf16 activations and of the float32 tolerance.
-__device__ __forceinline__ float erf_as(float z) {
-  const float az = fabsf(z);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, az, 1.0f));
-  float p = fmaf(t, 1.061405429f, -1.453152027f);
-  p = fmaf(t, p, 1.421413741f);
-  p = fmaf(t, p, -0.284496736f);
-  p = fmaf(t, p, 0.254829592f);
-  p *= t;
-  const float e = __builtin_amdgcn_exp2f(-(az * az) * 1.4426950408889634f);  // exp(-z^2)
-  const float r = fmaf(-p, e, 1.0f);
-  return copysignf(r, z);
-}
+// formula 7.1.26 (|error| <= 1.5e-7 for z >= 0):
+//   erfc(z) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2),
+//   t = 1 / (1 + p z),
+// with z = |x| / sqrt 2 folded into p and into the exponent, and the 1/2 into
+// the a_i.  About 12 VALU operations (two of them transcendental) per value,
+// less than half of a general-purpose erff.  |x| is capped at 2^16 in the
+// small term so that x = +inf gives +inf (that term is 0 there).
 __device__ __forceinline__ float gelu_erf(float x) {
-  const float hx = 0.5f * x;
-  return fmaf(hx, erf_as(x * 0.70710678118654752f), hx);
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.2316418882663604f, ax, 1.0f));  // p / sqrt 2
+  float q = fmaf(t, 0.5307027145f, -0.7265760135f);                              // a5/2, a4/2
+  q = fmaf(t, q, 0.7107068705f);                                                 // a3/2
+  q = fmaf(t, q, -0.142248368f);                                                 // a2/2
+  q = fmaf(t, q, 0.127414796f);                                                  // a1/2
+  const float w = (fminf(ax, 65536.0f) * t) * q;
+  const float e = __builtin_amdgcn_exp2f((x * x) * -0.7213475204444817f);       // exp(-x^2 / 2)
+  return fmaf(-w, e, fmaxf(x, 0.0f));
 }
 
 // ------------------------------------------------------------------ waves
