@@ -718,6 +718,40 @@ grouped_gemm_bf16_kernel(const GemmArgs a) {
   }
 }
 
+// sum[q] += slice sig's group q for sig = 0 .. split-1, in slice order:
+// slice sig's group q is at p + sig * slice_stride + q * q_stride (floats).
+// Two slices are loaded before either is added, so each round trip to
+// memory brings two slices.
+template <int QB>
+__device__ __forceinline__ void fixup_add_slices(float4* sum, const float* p, size_t q_stride, size_t slice_stride,
+                                                 int split) {
+  int sig = 0;
+  for (; sig + 1 < split; sig += 2) {
+    float4 t0[QB], t1[QB];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) t0[q] = *(const float4*)(p + sig * slice_stride + q * q_stride);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) t1[q] = *(const float4*)(p + (sig + 1) * slice_stride + q * q_stride);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      sum[q].x += t0[q].x; sum[q].y += t0[q].y; sum[q].z += t0[q].z; sum[q].w += t0[q].w;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      sum[q].x += t1[q].x; sum[q].y += t1[q].y; sum[q].z += t1[q].z; sum[q].w += t1[q].w;
+    }
+  }
+  if (sig < split) {
+    float4 t0[QB];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) t0[q] = *(const float4*)(p + sig * slice_stride + q * q_stride);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      sum[q].x += t0[q].x; sum[q].y += t0[q].y; sum[q].z += t0[q].z; sum[q].w += t0[q].w;
+    }
+  }
+}
+
 // Second pass of the tail split: adds the float32 partial sums of each
 // split tile in slice order and runs the epilogue.  Same launch shape as the
 // GEMM (it recomputes the same tail plan); workgroups without a tail tile
@@ -754,28 +788,20 @@ grouped_gemm_fixup_kernel(const GemmArgs a) {
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < NACC; ++v) acc[i][j][v] = 0.f;
-  // slice sums in slice order, 16-byte loads: per slice a batch of up to
-  // 16 groups (64 values) of this thread is loaded at once
+  // slice sums in slice order, 16-byte loads: a batch of up to 16 groups
+  // (64 values) of this thread from two slices at a time (the reduction is
+  // bound by load latency; split >= 2 whenever it runs)
   constexpr int NQ = FM * FN * NACC / 4;  // 16-byte groups per thread
   constexpr int QB = NQ < 16 ? NQ : 16;
   static_assert(NQ % QB == 0, "group batches");
   float4 sum[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) sum[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* part0 = a.partial + (size_t)(xcd + 8 * tau * tp.split) * (BM * BN);
 #pragma unroll
-  for (int q0 = 0; q0 < NQ; q0 += QB) {
-    for (int sig = 0; sig < tp.split; ++sig) {
-      const float* part = a.partial + (size_t)(xcd + 8 * (tau * tp.split + sig)) * (BM * BN);
-      float4 t[QB];
-#pragma unroll
-      for (int q = 0; q < QB; ++q) t[q] = *(const float4*)(part + ((size_t)(q0 + q) * NT + tid) * 4);
-#pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        sum[q0 + q].x += t[q].x; sum[q0 + q].y += t[q].y;
-        sum[q0 + q].z += t[q].z; sum[q0 + q].w += t[q].w;
-      }
-    }
-  }
+  for (int q0 = 0; q0 < NQ; q0 += QB)
+    fixup_add_slices<QB>(sum + q0, part0 + ((size_t)q0 * NT + tid) * 4, (size_t)NT * 4,
+                         (size_t)8 * (BM * BN), tp.split);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1097,18 +1123,19 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
 }
 
 // Second pass of the four-wave kernel's tail split, one single-wave
-// workgroup per 128 x 128 block of a tail tile: the reduction is bound by
-// load latency, so spreading a tile's four blocks over four compute units
-// shortens it.  Workgroup xcd + 8 (4 tau + q) takes block q (wave q of the
-// GEMM, wm = q / 2, wn = q % 2) of tail tile tau: it reads exactly the sums
-// that wave wrote, adds the slices in slice order and runs the same
-// epilogue, so the output is that of a whole-tile fixup.
+// workgroup per 32-row strip of each 128 x 128 block of a tail tile: the
+// reduction is bound by load latency, so spreading a tile over sixteen
+// compute units shortens it.  Workgroup xcd + 8 (16 tau + 4 q + i) takes
+// strip i (accumulator row i) of block q (wave q of the GEMM, wm = q / 2,
+// wn = q % 2) of tail tile tau: it reads exactly the sums that wave wrote
+// for that strip, adds the slices in slice order and runs the same epilogue
+// on the strip, so the output is that of a whole-tile fixup.
 template <int EPI>
 __global__ void __launch_bounds__(64) grouped_gemm_w4_fixup_kernel(const GemmArgs a) {
-  constexpr int BM = 256, BN = 256, NT = 256, MF = 32, FM = 4, FN = 4, NACC = 16;
-  constexpr int NQ = FM * FN * NACC / 4, QB = 16;  // 16-byte groups per thread, per batch
+  constexpr int BM = 256, BN = 256, NT = 256, MF = 32, FN = 4, NACC = 16;
+  constexpr int QS = FN * NACC / 4;  // 16-byte groups of one strip per thread
   const int lane = threadIdx.x;
-  const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3, tau = r >> 2, q = r & 3;
+  const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3, tau = r >> 4, q = (r >> 2) & 3, i = r & 3;
   const int nx = (a.grid - xcd + 7) >> 3;
   if (a.partial == nullptr || a.K / 64 < 16) return;
   const int m_used = rows_tiles_used<BM>(a);
@@ -1118,37 +1145,26 @@ __global__ void __launch_bounds__(64) grouped_gemm_w4_fixup_kernel(const GemmArg
   int n0, g, rows;
   if (!tile_coords<BM, BN, w4_band(EPI)>(a, m_used, tp.full_end + tau, row0, n0, g, rows)) return;
   const int wm = q >> 1, wn = q & 1;
-  if (wm * 128 >= rows) return;  // block wholly past the rows: nothing to store
+  if (wm * 128 + i * MF >= rows) return;  // strip wholly past the rows: nothing to store
   const int tid = q * 64 + lane;  // the GEMM thread whose sums these are
-  float4 sum[NQ];
+  float4 sum[QS];
 #pragma unroll
-  for (int k = 0; k < NQ; ++k) sum[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < QS; ++k) sum[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // the GEMM stored group k of accumulator (i, j) as group (i FN + j) NACC / 4 + k
+  const float* part0 = a.partial + (size_t)(xcd + 8 * tau * tp.split) * (BM * BN);
+  fixup_add_slices<QS>(sum, part0 + ((size_t)(i * QS) * NT + tid) * 4, (size_t)NT * 4, (size_t)8 * (BM * BN),
+                       tp.split);
+  f32x16_t acc[1][FN];
 #pragma unroll
-  for (int q0 = 0; q0 < NQ; q0 += QB) {
-    for (int sig = 0; sig < tp.split; ++sig) {
-      const float* part = a.partial + (size_t)(xcd + 8 * (tau * tp.split + sig)) * (BM * BN);
-      float4 t[QB];
+  for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int k = 0; k < QB; ++k) t[k] = *(const float4*)(part + ((size_t)(q0 + k) * NT + tid) * 4);
-#pragma unroll
-      for (int k = 0; k < QB; ++k) {
-        sum[q0 + k].x += t[k].x; sum[q0 + k].y += t[k].y;
-        sum[q0 + k].z += t[k].z; sum[q0 + k].w += t[k].w;
-      }
+    for (int v = 0; v < NACC / 4; ++v) {
+      const float4 u = sum[j * (NACC / 4) + v];
+      acc[0][j][4 * v] = u.x; acc[0][j][4 * v + 1] = u.y; acc[0][j][4 * v + 2] = u.z; acc[0][j][4 * v + 3] = u.w;
     }
-  }
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < NACC / 4; ++v) {
-        const float4 u = sum[(i * FN + j) * (NACC / 4) + v];
-        acc[i][j][4 * v] = u.x; acc[i][j][4 * v + 1] = u.y; acc[i][j][4 * v + 2] = u.z; acc[i][j][4 * v + 3] = u.w;
-      }
-  gemm_epilogue<BN, 2, 2, false, EPI, MF, FM, FN, NACC, false, false>(a, acc, g, rows, row0, n0, wm, wn, lane % MF,
-                                                                       lane / MF);
+  // the strip as a one-fragment wave tile: its rows start at (4 wm + i) * 32
+  gemm_epilogue<BN, 2, 2, false, EPI, MF, 1, FN, NACC, false, false>(a, acc, g, rows, row0, n0, 4 * wm + i, wn,
+                                                                      lane % MF, lane / MF);
 }
 
 // fp32 activations and weights: vector-ALU tiles (64 x 64 outputs, 4 x 4 per
@@ -1303,8 +1319,8 @@ hipError_t run_bf16_w4(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t part
   hipLaunchKernelGGL(grouped_gemm_bf16_w4_kernel<EPI>, dim3((unsigned)grid), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partial == nullptr) return e;
-  // the fixup: four single-wave workgroups per possible tail tile
-  hipLaunchKernelGGL(grouped_gemm_w4_fixup_kernel<EPI>, dim3((unsigned)grid * 4), dim3(64), 0, st, a);
+  // the fixup: sixteen single-wave workgroups per possible tail tile
+  hipLaunchKernelGGL(grouped_gemm_w4_fixup_kernel<EPI>, dim3((unsigned)grid * 16), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
