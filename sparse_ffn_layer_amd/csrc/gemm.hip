@@ -1360,9 +1360,13 @@ static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hi
       // share each weight panel through L2 (fp8-weight DeepSeek shape, W8A8:
       // 2.53 -> 2.39 ms/step against bands of 2 consecutive row tiles)
       if constexpr (BFP8) {
-        // fp8 weights: k stages of 128, so each stage reads whole 128-byte
-        // lines of every weight row (W8A16 DeepSeek shape 3.47 -> 3.31
-        // ms/step against stages of 64 with three slots)
+        // fp8 weights with bf16 rows: 512-wide tiles read each activation
+        // row half as often (the larger share of these products' L1 -> L2
+        // requests), at the price of k stages of 64 (W8A16 DeepSeek shape:
+        // expert_up 1.42-1.46 -> 1.42 ms, expert_down 1.44 -> 1.40 ms);
+        // else k stages of 128, so each stage reads whole 128-byte lines of
+        // every weight row (3.47 -> 3.31 ms/step against stages of 64)
+        if (a.N % 512 == 0) return run_bf16<128, 512, 64, 2, 4, 3, true, EPI, -4, 32>(a, rows_cap, st, pb);
         if (n256 && k128) return run_bf16<128, 256, 128, 2, 4, 2, true, EPI, -4, 32>(a, rows_cap, st, pb);
       }
       if (n256) return run_bf16<128, 256, 64, 2, 4, 3, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);
@@ -1396,7 +1400,7 @@ size_t expert_split_bytes(const Problem& p) {
   if (p.act == DT_F32) return 0;
   switch (gemm_regime(p)) {
     case 0: return (size_t)kSplitGrid * 256 * 256 * sizeof(float);
-    case 1: return (size_t)kSplitGrid * 128 * 256 * sizeof(float);
+    case 1: return (size_t)kSplitGrid * 128 * 256 * sizeof(float);  // also 256 workgroups of 128 x 512
     default: return 0;
   }
 }
