@@ -174,6 +174,40 @@ def _act(p: moe_problem):
     return _ACT_TORCH[p.act_dtype]
 
 
+_ESZ = {MOE_F32: 4, MOE_BF16: 2, MOE_FP8_E4M3: 1}
+
+
+def _need_bytes(p: moe_problem, name: str) -> int:
+    """Bytes the argument `name` of an entry point spans for problem p (the
+    shapes include/moe.h states)."""
+    S, d, d_ff, E, K = int(p.S), int(p.d), int(p.d_ff), int(p.E), int(p.K)
+    a, w = _ESZ[p.act_dtype], _ESZ[p.w_dtype]
+    rows = moe_rows_capacity(p) if name in ("x_perm", "h", "y_perm", "x8", "x_scale", "h8", "h_scale") else 0
+    return {
+        "x": S * d * a, "W_r": E * d * a, "router_bias": E * 4, "select_bias": E * 4,
+        "logits_in": S * E * 4, "logits_out": S * E * 4, "logits": S * E * 4,
+        "topk_idx": S * K * 4, "topk_gate": S * K * 4, "topk_idx_out": S * K * 4, "topk_gate_out": S * K * 4,
+        "perm": S * K * 4, "inv_perm": S * K * 4,
+        "expert_counts": E * 4, "expert_counts_out": E * 4, "expert_offsets": (E + 1) * 4,
+        "x_perm": rows * d * a, "h": rows * d_ff * a, "y_perm": rows * d * a,
+        "x8": rows * d, "x_scale": rows * 4, "h8": rows * d_ff, "h_scale": rows * 4,
+        "W1": E * d_ff * d * w, "W2": E * d * d_ff * w, "b1": E * d_ff * a, "b2": E * d * a,
+        "w1_scale": E * d_ff * 4, "w2_scale": E * d * 4, "y": S * d * a,
+        "stats": MOE_STATS_N * 4, "dropped": 4,
+    }[name]
+
+
+def _check_sizes(fn: str, p: moe_problem, **tensors) -> None:
+    """The library takes plain pointers: a tensor smaller than its argument's
+    extent would be read or written past its end.  Raise instead."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        have, need = t.numel() * t.element_size(), _need_bytes(p, name)
+        if have < need:
+            raise ValueError(f"{fn}: {name} holds {have} bytes, the problem needs {need}")
+
+
 # ------------------------------------------------------------------ entry points
 def moe_route(p, x, W_r, router_bias=None, select_bias=None, logits_in=None, logits_out=None,
               topk_idx=None, topk_gate=None, ws=None, stream=None):
@@ -185,6 +219,9 @@ def moe_route(p, x, W_r, router_bias=None, select_bias=None, logits_in=None, log
         topk_gate = _empty((p.S, p.K), torch.float32, dev, side)
     if ws is None:
         ws = workspace(p, STAGE_ROUTE, dev, side)
+    _check_sizes("moe_route", p, x=None if logits_in is not None else x,
+                 W_r=None if logits_in is not None else W_r, router_bias=router_bias, select_bias=select_bias,
+                 logits_in=logits_in, logits_out=logits_out, topk_idx=topk_idx, topk_gate=topk_gate)
     st = lib().moe_route(ctypes.byref(p), _ptr(x), _ptr(W_r), _ptr(router_bias), _ptr(select_bias),
                          _ptr(logits_in), _ptr(logits_out), _ptr(topk_idx), _ptr(topk_gate),
                          _ptr(ws), ws.numel(), _stream(stream))
@@ -205,6 +242,8 @@ def moe_permute(p, topk_idx, x, expert_counts=None, expert_offsets=None, perm=No
         x_perm = _empty((moe_rows_capacity(p), p.d), _act(p), dev, side)
     if ws is None:
         ws = workspace(p, STAGE_PERMUTE, dev, side)
+    _check_sizes("moe_permute", p, topk_idx=topk_idx, x=x, expert_counts=expert_counts,
+                 expert_offsets=expert_offsets, perm=perm, inv_perm=inv_perm, x_perm=x_perm)
     st = lib().moe_permute(ctypes.byref(p), _ptr(topk_idx), _ptr(x), _ptr(expert_counts),
                            _ptr(expert_offsets), _ptr(perm), _ptr(inv_perm), _ptr(x_perm),
                            _ptr(ws), ws.numel(), _stream(stream))
@@ -221,6 +260,8 @@ def moe_expert_ffn(p, x_perm, expert_counts, expert_offsets, W1, b1, W2, b2, w1_
     y_perm = _empty((cap, p.d), _act(p), dev, side) if y_perm is None else y_perm
     if ws is None:
         ws = workspace(p, STAGE_EXPERT_FFN, dev, side)
+    _check_sizes("moe_expert_ffn", p, x_perm=x_perm, expert_counts=expert_counts, expert_offsets=expert_offsets,
+                 W1=W1, b1=b1, W2=W2, b2=b2, w1_scale=w1_scale, w2_scale=w2_scale, h=h, y_perm=y_perm)
     st = lib().moe_expert_ffn(ctypes.byref(p), _ptr(x_perm), _ptr(expert_counts), _ptr(expert_offsets),
                               _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(w1_scale), _ptr(w2_scale),
                               _ptr(h), _ptr(y_perm), _ptr(ws), ws.numel(), _stream(stream))
@@ -235,6 +276,8 @@ def moe_expert_up(p, x_perm, expert_counts, expert_offsets, W1, b1, w1_scale=Non
         h = _empty((moe_rows_capacity(p), p.d_ff), _act(p), x_perm.device, side)
     if ws is None:
         ws = workspace(p, STAGE_EXPERT_FFN, x_perm.device, side)
+    _check_sizes("moe_expert_up", p, x_perm=x_perm, expert_counts=expert_counts, expert_offsets=expert_offsets,
+                 W1=W1, b1=b1, w1_scale=w1_scale, h=h)
     st = lib().moe_expert_up(ctypes.byref(p), _ptr(x_perm), _ptr(expert_counts), _ptr(expert_offsets),
                              _ptr(W1), _ptr(b1), _ptr(w1_scale), _ptr(h), _ptr(ws), ws.numel(),
                              _stream(stream))
@@ -249,6 +292,8 @@ def moe_expert_down(p, h, expert_counts, expert_offsets, W2, b2, w2_scale=None, 
         y_perm = _empty((moe_rows_capacity(p), p.d), _act(p), h.device, side)
     if ws is None:
         ws = workspace(p, STAGE_EXPERT_FFN, h.device, side)
+    _check_sizes("moe_expert_down", p, h=h, expert_counts=expert_counts, expert_offsets=expert_offsets,
+                 W2=W2, b2=b2, w2_scale=w2_scale, y_perm=y_perm)
     st = lib().moe_expert_down(ctypes.byref(p), _ptr(h), _ptr(expert_counts), _ptr(expert_offsets),
                                _ptr(W2), _ptr(b2), _ptr(w2_scale), _ptr(y_perm), _ptr(ws), ws.numel(),
                                _stream(stream))
@@ -264,6 +309,8 @@ def moe_expert_up_a8(p, x8, x_scale, expert_counts, expert_offsets, W1, b1, w1_s
         h = _empty((moe_rows_capacity(p), p.d_ff), torch.bfloat16, x8.device, side)
     if ws is None:
         ws = workspace(p, STAGE_EXPERT_FFN, x8.device, side)
+    _check_sizes("moe_expert_up_a8", p, x8=x8, x_scale=x_scale, expert_counts=expert_counts,
+                 expert_offsets=expert_offsets, W1=W1, b1=b1, w1_scale=w1_scale, h=h)
     st = lib().moe_expert_up_a8(ctypes.byref(p), _ptr(x8), _ptr(x_scale), _ptr(expert_counts),
                                 _ptr(expert_offsets), _ptr(W1), _ptr(b1), _ptr(w1_scale), _ptr(h), _ptr(ws),
                                 ws.numel(), _stream(stream))
@@ -279,6 +326,8 @@ def moe_expert_down_a8(p, h8, h_scale, expert_counts, expert_offsets, W2, b2, w2
         y_perm = _empty((moe_rows_capacity(p), p.d), torch.bfloat16, h8.device, side)
     if ws is None:
         ws = workspace(p, STAGE_EXPERT_FFN, h8.device, side)
+    _check_sizes("moe_expert_down_a8", p, h8=h8, h_scale=h_scale, expert_counts=expert_counts,
+                 expert_offsets=expert_offsets, W2=W2, b2=b2, w2_scale=w2_scale, y_perm=y_perm)
     st = lib().moe_expert_down_a8(ctypes.byref(p), _ptr(h8), _ptr(h_scale), _ptr(expert_counts),
                                   _ptr(expert_offsets), _ptr(W2), _ptr(b2), _ptr(w2_scale), _ptr(y_perm),
                                   _ptr(ws), ws.numel(), _stream(stream))
@@ -289,6 +338,7 @@ def moe_expert_down_a8(p, h8, h_scale, expert_counts, expert_offsets, W2, b2, w2
 def moe_combine(p, y_perm, inv_perm, topk_gate, y=None, stream=None):
     if y is None:
         y = _empty((p.S, p.d), _act(p), y_perm.device, _side(stream))
+    _check_sizes("moe_combine", p, y_perm=y_perm, inv_perm=inv_perm, topk_gate=topk_gate, y=y)
     st = lib().moe_combine(ctypes.byref(p), _ptr(y_perm), _ptr(inv_perm), _ptr(topk_gate), _ptr(y),
                            _stream(stream))
     _check("moe_combine", st)
@@ -303,6 +353,9 @@ def moe_layer_forward(p, x, W_r, W1, b1, W2, b2, router_bias=None, select_bias=N
         y = _empty((p.S, p.d), _act(p), x.device, side)
     if ws is None:
         ws = workspace(p, STAGE_LAYER, x.device, side)
+    _check_sizes("moe_layer_forward", p, x=x, W_r=W_r, router_bias=router_bias, select_bias=select_bias, W1=W1,
+                 b1=b1, W2=W2, b2=b2, w1_scale=w1_scale, w2_scale=w2_scale, y=y, topk_idx_out=topk_idx_out,
+                 topk_gate_out=topk_gate_out, logits_out=logits_out, expert_counts_out=expert_counts_out)
     st = lib().moe_layer_forward(ctypes.byref(p), _ptr(x), _ptr(W_r), _ptr(router_bias),
                                  _ptr(select_bias), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
                                  _ptr(w1_scale), _ptr(w2_scale), _ptr(y), _ptr(topk_idx_out),
@@ -317,6 +370,9 @@ def moe_layer_forward_noalloc(p, x, W_r, W1, b1, W2, b2, y, router_bias=None, se
                               logits_out=None, expert_counts_out=None, stream=None):
     """moe_layer_forward on the library's own scratch array: the caller passes
     every input and output (y included) and nothing is allocated."""
+    _check_sizes("moe_layer_forward_noalloc", p, x=x, W_r=W_r, router_bias=router_bias, select_bias=select_bias,
+                 W1=W1, b1=b1, W2=W2, b2=b2, w1_scale=w1_scale, w2_scale=w2_scale, y=y, topk_idx_out=topk_idx_out,
+                 topk_gate_out=topk_gate_out, logits_out=logits_out, expert_counts_out=expert_counts_out)
     st = lib().moe_layer_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(W_r), _ptr(router_bias),
                                          _ptr(select_bias), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
                                          _ptr(w1_scale), _ptr(w2_scale), _ptr(y), _ptr(topk_idx_out),
@@ -333,6 +389,7 @@ def moe_load_stats(p, expert_counts, logits=None, dropped=None, alpha=1.0, stats
         # every entry is written by the kernel: no fill on the current stream
         # that could race with a launch on another one
         stats = _empty(MOE_STATS_N, torch.float32, expert_counts.device, _side(stream))
+    _check_sizes("moe_load_stats", p, expert_counts=expert_counts, logits=logits, dropped=dropped, stats=stats)
     st = lib().moe_load_stats(ctypes.byref(p), _ptr(expert_counts), _ptr(logits), _ptr(dropped),
                               float(alpha), _ptr(stats), _stream(stream))
     _check("moe_load_stats", st)
@@ -350,6 +407,8 @@ def moe_apply_capacity(p, logits, topk_idx, select_bias=None, topk_gate=None, dr
         dropped = _empty(4, torch.int32, topk_idx.device, side)  # entry 0 is written by the kernel
     if ws is None:
         ws = workspace(p, STAGE_CAPACITY, topk_idx.device, side)
+    _check_sizes("moe_apply_capacity", p, logits=logits, select_bias=select_bias, topk_idx=topk_idx,
+                 topk_gate=topk_gate, dropped=dropped)
     st = lib().moe_apply_capacity(ctypes.byref(p), _ptr(logits), _ptr(select_bias), _ptr(topk_idx),
                                   _ptr(topk_gate), _ptr(dropped), _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_apply_capacity", st)
@@ -365,6 +424,8 @@ def moe_quantize_rows(src, codes=None, scales=None, stream=None):
         codes = _empty((rows, n), torch.uint8, src.device, side)
     if scales is None:
         scales = _empty(max(rows, 1), torch.float32, src.device, side)
+    if codes.numel() * codes.element_size() < rows * n or scales.numel() * scales.element_size() < rows * 4:
+        raise ValueError(f"moe_quantize_rows: codes need {rows * n} bytes and scales {rows * 4} for {rows} rows")
     st = lib().moe_quantize_rows(_ptr(src), int(rows), int(n), _ptr(codes), _ptr(scales), _stream(stream))
     _check("moe_quantize_rows", st)
     return codes, scales[:rows]
