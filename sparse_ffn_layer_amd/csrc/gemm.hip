@@ -753,26 +753,28 @@ __device__ __forceinline__ void fixup_add_slices(float4* sum, const float* p, si
 }
 
 // Second pass of the tail split: adds the float32 partial sums of each
-// split tile in slice order and runs the epilogue.  Same launch shape as the
-// GEMM (it recomputes the same tail plan); workgroups without a tail tile
-// return at once.
+// split tile in slice order and runs the epilogue.  It recomputes the GEMM's
+// tail plan; workgroups without a tail tile return at once.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool BFP8, int EPI, int GM, int MF, bool A8 = false>
-__global__ void __launch_bounds__(64 * WM * WN)
+__global__ void __launch_bounds__(64)
 grouped_gemm_fixup_kernel(const GemmArgs a) {
-  constexpr int NT = 64 * WM * WN;
+  // One single-wave workgroup per wave of each tail tile (the reduction is
+  // bound by load latency, so spreading a tile over WM WN compute units
+  // shortens it): workgroup xcd + 8 (NW tau + w) takes wave w's sums of tail
+  // tile tau, exactly what that wave of the GEMM wrote.
+  constexpr int NT = 64 * WM * WN, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / MF, FN = WTN / MF;
   constexpr int NACC = MF == 16 ? 4 : 16;
   typedef typename std::conditional<MF == 16, f32x4_t, f32x16_t>::type acc_t;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x;
+  const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3, tau = r / NW, wave = r % NW;
+  const int tid = wave * 64 + lane;  // the GEMM thread whose sums these are
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane % MF, lk = lane / MF;
   const int m_used = rows_tiles_used<BM>(a);
   const int64_t T = (int64_t)m_used * a.n_tiles;
   const int nwg = a.grid;
-  const int xcd = blockIdx.x & 7, tau = blockIdx.x >> 3;
   const int nx = (nwg - xcd + 7) >> 3;
   if (a.partial == nullptr || a.K / BK < 16) return;
   const TailPlan tp = tail_plan(T, xcd, nx, true);
@@ -781,6 +783,7 @@ grouped_gemm_fixup_kernel(const GemmArgs a) {
   int n0, g, rows;
   constexpr int BAL_FR = GM < 0 ? MF : 0;  // balanced row tiles, as in the GEMM
   if (!tile_coords<BM, BN, GM, BAL_FR>(a, m_used, tp.full_end + tau, row0, n0, g, rows)) return;
+  if (wm * WTM >= rows) return;  // this wave's rows are all past the tile's rows: nothing to store
   acc_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -1298,7 +1301,7 @@ hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partial == nullptr) return e;
   hipLaunchKernelGGL((grouped_gemm_fixup_kernel<BM, BN, BK, WM, WN, STAGES, BFP8, EPI, GM, MF, A8>),
-                     dim3((unsigned)grid), dim3(NT), 0, st, a);
+                     dim3((unsigned)grid * (NT / 64)), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
