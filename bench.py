@@ -228,12 +228,12 @@ def pmc_probe(a, D, M, torch):
 def gemm_kernel_stage(k):
     """(stage, fp8 activations?) of an expert GEMM kernel name, or None.  The
     epilogue (0: bias + GeLU = expert_up, 1: bias = expert_down) is the only
-    template argument of the four-wave kernel and the eighth of the general
+    template argument of the eight-wave kernel and the eighth of the general
     one, whose eleventh says whether the activations are e4m3."""
     if "grouped_gemm_bf16" not in k or "fixup" in k or "<" not in k:
         return None
     args = [x.strip() for x in k.split("<", 1)[1].split(">", 1)[0].split(",")]
-    epi = args[0] if "_w4_kernel" in k else args[7]
+    epi = args[0] if "_w8_kernel" in k else args[7]
     if epi not in ("0", "1"):
         return None
     a8 = len(args) > 10 and args[10] == "true"

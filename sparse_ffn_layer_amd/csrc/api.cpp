@@ -112,7 +112,7 @@ int64_t rows_capacity(const Problem& p) {
 // The layer's up product reads the token rows of x (or, W8A8, their e4m3
 // codes) in place through a row -> token map written by the permute, instead
 // of a gathered x_perm, when its kernel can (bf16 activations, not the
-// four-wave prefill kernel) and the source fits one 32-bit buffer range.
+// eight-wave prefill kernel) and the source fits one 32-bit buffer range.
 bool in_place_rows(const Problem& p) {
   const int64_t asz = p.act_quant ? 1 : 2;
   return expert_up_reads_in_place(p) && (p.S + 1) * (int64_t)p.d * asz < (int64_t(1) << 32);

@@ -817,38 +817,63 @@ grouped_gemm_fixup_kernel(const GemmArgs a) {
   gemm_epilogue<BN, WM, WN, BFP8, EPI, MF, FM, FN, NACC, false, A8>(a, acc, g, rows, row0, n0, wm, wn, lr, lk);
 }
 
-// Epilogue of the four-wave kernel, through LDS: bias (+ GeLU) and bf16
-// rounding in the MFMA layout, into a per-wave 128 x 128 tile in LDS (16-byte
-// chunk c of row r at slot c ^ (r & 15)), then stored by whole 256-byte row
-// segments (16 lanes per row, 4 rows per store instruction) instead of 16-byte
-// pieces of 32 rows.  The bias of all the lane's channels is loaded first so
-// the loads overlap.  The caller has made every wave finish with the k-stages
-// in LDS.
+// bf16 prefill tiles of 256 x 256 with eight waves, two per SIMD, each
+// owning 128 rows x 64 channels: 8 accumulator blocks of 32 x 32 in AGPRs
+// (128 registers), so the two waves of a SIMD fit its register file and one
+// issues MFMAs while the other waits on LDS or on the vector-memory queue.
+// Every 16-byte fragment read from LDS feeds two (A) or four (B) MFMAs.
+//
+// The tile's global loads are staged in VGPRs: stage kt + 2 is loaded during
+// stage kt and written to LDS during stage kt + 1, into the slot that the
+// barrier ending stage kt freed.  Every k-step interleaves its LDS reads, LDS
+// writes and global loads with the MFMAs, at most one of each per MFMA; the
+// loads of a stage are spread over two k-steps.  The last stage of a tile
+// loads the next tile's first stage the same way, so those loads fly during
+// the epilogue.  Rows of a partly filled tile do all MFMAs (their loads read
+// zeros); only the stores skip them.  Row tiles are balanced as in the
+// general kernel, whose split-K fixup reduces the tail: the partial sums are
+// laid out as that kernel's with 2 x 4 waves of 128 x 64.
+//
+// Against the 256 x 256 tile on four waves of 128 x 128 (one per SIMD, all
+// 512 registers each) that preceded it: Mixtral shape expert_up 0.92-0.93 ->
+// 0.89-0.92 ms, expert_down 0.84-0.86 -> 0.84-0.85 ms, layer 1.85-1.87 ->
+// 1.82-1.84 ms/step; Zipf shape 1.76 -> 1.72-1.75 ms/step.
+//
+// Bands of the tile order: expert-aligned, up to 8 row tiles (each band
+// re-reads the weights of its expert once; against bands of 8 (up) and 4
+// (down) consecutive row tiles of the whole tile space: Mixtral shape 1.96 ->
+// 1.94 ms/step, Zipf shape 1.86 -> 1.82 ms/step; bands of 4 or 16 expert row
+// tiles measured no better).
+constexpr int kW8Band = -8;
+
+// Epilogue of the eight-wave kernel, through LDS: bias (+ GeLU) and bf16
+// rounding in the MFMA layout, into a per-wave 128 x 64 tile in LDS (16-byte
+// chunk c of row r at slot c ^ (r & 7)), then stored by whole 128-byte row
+// segments (8 lanes per row, 8 rows per store instruction) instead of 8-byte
+// pieces of 32 rows.  The caller has made every wave finish with the
+// k-stages in LDS.
 template <int EPI>
-__device__ __forceinline__ void w4_epilogue(const GemmArgs& a, const f32x16_t (&acc)[4][4], int g, int rows,
+__device__ __forceinline__ void w8_epilogue(const GemmArgs& a, const f32x16_t (&acc)[4][2], int g, int rows,
                                             int64_t row0, int n0, int wm, int wn, int lr, int lk, int lane, char* wt) {
   asm volatile("" : "+v"(lr), "+v"(lk));  // addresses computed here, not hoisted into the main loop
-  uint2 bias[4][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j) {
+    uint2 bias[4];  // one block's channels at a time (registers are scarce with two waves per SIMD)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int n = n0 + wn * 128 + j * 32 + q4 * 8 + lk * 4;
-      bias[j][q4] = a.bias != nullptr ? *(const uint2*)((const uint16_t*)a.bias + (int64_t)g * a.N + n) : make_uint2(0, 0);
+      const int n = n0 + wn * 64 + j * 32 + q4 * 8 + lk * 4;
+      bias[q4] = a.bias != nullptr ? *(const uint2*)((const uint16_t*)a.bias + (int64_t)g * a.N + n) : make_uint2(0, 0);
     }
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      // one group of accumulators at a time (read from AGPRs where used)
       __builtin_amdgcn_sched_barrier(0);
-      const uint2 b2 = bias[j][q4];
+      const uint2 b2 = bias[q4];
       const float bi[4] = {bf16_bits_to_f32(b2.x & 0xffff), bf16_bits_to_f32(b2.x >> 16),
                            bf16_bits_to_f32(b2.y & 0xffff), bf16_bits_to_f32(b2.y >> 16)};
-      const int cc = j * 4 + q4;  // 16-byte chunk of the wave tile's row: channels 8 cc .. 8 cc + 7
+      const int cc = j * 4 + q4;  // 16-byte chunk of the wave tile's row (8 per row)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (wm * 128 + i * 32 >= rows) continue;  // uniform: fragment wholly past the rows
+        if (wm * 128 + i * 32 >= rows) continue;
         const int r = i * 32 + lr;
         float v[4];
 #pragma unroll
@@ -857,56 +882,37 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& a, const f32x16_t (&
           if constexpr (EPI == EPI_GELU) t = gelu_erf(t);
           v[q] = t;
         }
-        *(uint2*)(wt + r * 256 + ((cc ^ (r & 15)) << 4) + lk * 8) =
+        *(uint2*)(wt + r * 128 + ((cc ^ (r & 7)) << 4) + lk * 8) =
             make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
-  wait_lgkmcnt<0>();  // the wave reads back only its own tile
-  const int c = lane & 15;
+  }
+  wait_lgkmcnt<0>();
+  const int c = lane & 7;
 #pragma unroll 4
-  for (int rr = 0; rr < 128; rr += 4) {
-    const int r = rr + (lane >> 4);
-    const uint4 val = *(const uint4*)(wt + r * 256 + ((c ^ (r & 15)) << 4));
+  for (int rr = 0; rr < 128; rr += 8) {
+    const int r = rr + (lane >> 3);
+    const uint4 val = *(const uint4*)(wt + r * 128 + ((c ^ (r & 7)) << 4));
     const int m = wm * 128 + r;
-    if (m < rows) *(uint4*)((uint16_t*)a.C + (row0 + m) * a.ldc + n0 + wn * 128 + c * 8) = val;
+    if (m < rows) *(uint4*)((uint16_t*)a.C + (row0 + m) * a.ldc + n0 + wn * 64 + c * 8) = val;
   }
 }
 
-// bf16 prefill tiles of 256 x 256 with four waves (one per SIMD), each wave
-// owning a 128 x 128 quarter: 16 accumulator blocks of 32 x 32 in AGPRs (all
-// 256), so every 16-byte fragment read from LDS feeds four MFMAs.
-//
-// The tile's global loads are staged in VGPRs: stage kt + 2 is loaded during
-// stage kt and written to LDS during stage kt + 1, into the slot that the
-// barrier ending stage kt freed.  Every k-step interleaves its LDS reads, LDS
-// writes and global loads one or two per MFMA; the loads of a stage are
-// spread over three k-steps, since a burst of them stalls in-order issue
-// behind the vector-memory queue and with one wave per SIMD nothing else
-// fills the MFMA pipe meanwhile.  The last stage of a tile loads the next
-// tile's first stage the same way, so those loads fly during the epilogue.
-// Rows of a partly filled tile do all MFMAs (their loads read zeros); only
-// the stores skip them.
-// Bands of the four-wave kernel's tile order: expert-aligned, up to 8 row
-// tiles (each band re-reads the weights of its expert once; against bands
-// of 8 (up) and 4 (down) consecutive row tiles of the whole tile space:
-// Mixtral shape 1.96 -> 1.94 ms/step, Zipf shape 1.86 -> 1.82 ms/step).
-constexpr int w4_band(int) { return -8; }
-
 template <int EPI>
-__global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const GemmArgs a) {
-  constexpr int BM = 256, BN = 256, BK = 64, NT = 256, GM = w4_band(EPI), MF = 32;
-  constexpr int CA = BK * 2 / 16;  // 16-byte chunks per row
+__global__ void __launch_bounds__(512, 1) grouped_gemm_bf16_w8_kernel(const GemmArgs a) {
+  constexpr int BM = 256, BN = 256, BK = 64, NT = 512, GM = kW8Band, MF = 32, WN = 4;
+  constexpr int CA = BK * 2 / 16;
   constexpr int A_BYTES = BM * BK * 2, STAGE_BYTES = A_BYTES + BN * BK * 2;
   constexpr int A_LOADS = BM * CA / NT, B_LOADS = BN * CA / NT, LOADS = A_LOADS + B_LOADS;
-  constexpr int FM = 4, FN = 4, NACC = 16, KS = BK / 16, KC = 2, NMF = FM * FN;
-  static_assert(LOADS == 16 && NMF == 16, "the k-step schedule below assumes 16 loads and 16 MFMAs");
-  static_assert(2 * STAGE_BYTES >= 4 * 128 * 256, "the epilogue's per-wave tiles fit in the stage buffers");
+  constexpr int FM = 4, FN = 2, NACC = 16, KS = BK / 16, KC = 2, NMF = FM * FN;
+  static_assert(LOADS == 8 && NMF == 8, "the k-step schedule below assumes 8 loads and 8 MFMAs");
+  static_assert(2 * STAGE_BYTES >= 8 * 128 * 128, "the epilogue's per-wave tiles fit in the stage buffers");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lk = lane >> 5;
 
   const int m_used = rows_tiles_used<BM>(a);
@@ -917,18 +923,14 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
   const int KT_ALL = a.K / BK;
   const TailPlan tp = tail_plan(T, xcd, nx, a.partial != nullptr && KT_ALL >= 16);
 
-  // Work item k of this workgroup: whole tiles of the full rounds, then
-  // (with a split) one k-slice of a tail tile.  (No rows read in place here:
-  // the item's offsets would not fit the registers this kernel has left.)
   struct Item {
     int64_t row0;
     int n0, g, rows, kt0, kt1;
     float* part;
-    i32x4_t ra, rb;  // buffer resources of the tile's A rows and B rows
+    i32x4_t ra, rb;
   };
   const int64_t loop_end = tp.split ? tp.full_end : tp.t_hi;
   const bool has_slice = tp.split && xj < tp.tail * tp.split;
-  // the first valid item at index >= k (k is advanced past it)
   auto next_item = [&](int& k, Item& it) -> bool {
     for (;; ++k) {
       const int64_t L = tp.t_lo + xj + (int64_t)k * nx;
@@ -937,17 +939,14 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
       it.kt1 = KT_ALL;
       it.part = nullptr;
       if (L >= loop_end) {
-        if (!has_slice || L - nx >= loop_end) return false;  // the slice comes once, after the whole tiles
+        if (!has_slice || L - nx >= loop_end) return false;
         const int tau = xj / tp.split, sig = xj % tp.split;
         Lt = tp.full_end + tau;
         it.kt0 = KT_ALL * sig / tp.split;
         it.kt1 = KT_ALL * (sig + 1) / tp.split;
         it.part = a.partial + (size_t)blockIdx.x * (BM * BN);
       }
-      if (!tile_coords<BM, BN, GM>(a, m_used, Lt, it.row0, it.n0, it.g, it.rows)) continue;
-      // exact ranges: chunks of rows past the group's count are dropped (zeros,
-      // no access).  The values are wave-uniform; readfirstlane says so, so
-      // the resources stay in SGPRs (a buffer load needs them there).
+      if (!tile_coords<BM, BN, GM, MF>(a, m_used, Lt, it.row0, it.n0, it.g, it.rows)) continue;
       auto uni = [](i32x4_t v) {
         return i32x4_t{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
                        __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w)};
@@ -960,50 +959,42 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
     }
   };
 
-  // per-thread chunk offsets (the same for every tile); same XOR-swizzled
-  // LDS layout as the kernel above
-  uint32_t a_off[A_LOADS], b_off[B_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int q = i * NT + tid, r = q / CA, s = q % CA;
-    a_off[i] = (uint32_t)(r * a.lda * 2 + (s ^ swz<CA>(r)) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int q = i * NT + tid, r = q / CA, s = q % CA;
-    b_off[i] = (uint32_t)(r * a.ldb * 2 + (s ^ swz<CA>(r)) * 16);
-  }
+  // chunk l of this thread: row l * (NT / CA) + tid / CA, chunk tid % CA;
+  // the swizzle depends on the row only through bits that l does not touch,
+  // so one offset per operand and a uniform row stride cover all loads
+  static_assert((NT / CA) % 32 == 0, "row stride keeps the swizzle bits");
+  // (A and B rows both hold the K contraction values: lda == ldb, checked
+  // by the launcher, so one offset serves both operands)
+  const int r0 = tid / CA, s0 = tid % CA;
+  const uint32_t g_off0 = (uint32_t)(r0 * a.lda * 2 + (s0 ^ swz<CA>(r0)) * 16);
+  const uint32_t g_step = (uint32_t)((NT / CA) * a.lda * 2);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  uint32_t a_rd[FM], b_rd[FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int r = wm * 128 + i * MF + lr;
-    a_rd[i] = lds0 + (uint32_t)(r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
-  }
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int r = wn * 128 + j * MF + lr;
-    b_rd[j] = lds0 + (uint32_t)(A_BYTES + r * CA * 16 + ((lk ^ swz<CA>(r)) << 4));
-  }
-  i32x4_t R[LOADS];  // one stage of a tile (this thread's 16 chunks)
+  // fragment i of A / j of B: rows 32 apart, the same swizzle (32, 64 and
+  // 128 rows keep bits 0-4 of the row), so one lane address plus uniform
+  // offsets: wave row / column base, then 32 * CA * 16 bytes per fragment
+  const uint32_t rd0 = lds0 + (uint32_t)(lr * CA * 16 + ((lk ^ swz<CA>(lr)) << 4));
+  const uint32_t a_base = (uint32_t)(wm * 128 * CA * 16), b_base = (uint32_t)(A_BYTES + wn * 64 * CA * 16);
+  constexpr uint32_t FRAG_STEP = MF * CA * 16;
+  i32x4_t R[LOADS];
   auto gload = [&](const Item& it, int kt, int l) {
     const uint32_t ko = (uint32_t)((it.kt0 + kt) * BK * 2);
-    R[l] = l < A_LOADS ? buffer_load_16(it.ra, a_off[l], ko) : buffer_load_16(it.rb, b_off[l - A_LOADS], ko);
+    R[l] = l < A_LOADS ? buffer_load_16(it.ra, g_off0 + (uint32_t)l * g_step, ko)
+                       : buffer_load_16(it.rb, g_off0 + (uint32_t)(l - A_LOADS) * g_step, ko);
   };
   auto swrite = [&](int slot, int l) {
     char* base = smem + slot * STAGE_BYTES + (l < A_LOADS ? 0 : A_BYTES);
     const int ll = l < A_LOADS ? l : l - A_LOADS;
     *(i32x4_t*)(base + (ll * NT + tid) * 16) = R[l];
   };
-  // fragment q of k-step ks (q < FM: A fragment q, else B fragment q - FM)
   auto read_one = [&](int slot, int ks, int q, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
     const uint32_t so = (uint32_t)(slot * STAGE_BYTES), kx = (uint32_t)((KC * ks) << 4);
-    if (q < FM) asm volatile("ds_read_b128 %0, %1" : "=v"(af[q]) : "v"((a_rd[q] ^ kx) + so));
-    else asm volatile("ds_read_b128 %0, %1" : "=v"(bf[q - FM]) : "v"((b_rd[q - FM] ^ kx) + so));
+    if (q < FM)
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(af[q]) : "v"((rd0 ^ kx) + so + a_base), "n"(q * FRAG_STEP));
+    else
+      asm volatile("ds_read_b128 %0, %1 offset:%2"
+                   : "=v"(bf[q - FM]) : "v"((rd0 ^ kx) + so + b_base), "n"((q - FM) * FRAG_STEP));
   };
 
-  // one tile; pre: its stage 0 is already in R; has_next: the last stage
-  // loads stage 0 of `nit` (the next item) into R
   auto run_tile = [&](const Item& it, bool pre, bool has_next, const Item& nit) {
     f32x16_t acc[FM][FN];
 #pragma unroll
@@ -1012,15 +1003,12 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < NACC; ++v) acc[i][j][v] = 0.f;
-    // wait states between the VALU writes of the zeroed AGPRs and the first
-    // MFMA reading them as its C operand
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 4" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
     const int KT = it.kt1 - it.kt0;
-    __syncthreads();  // every wave is done with the previous tile's LDS
-    // prologue: stage 0 to slot 0, stage 1 into the registers
+    __syncthreads();
     if (!pre) {
 #pragma unroll
       for (int l = 0; l < LOADS; ++l) gload(it, 0, l);
@@ -1036,10 +1024,6 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
 #pragma unroll
     for (int q = 0; q < FM + FN; ++q) read_one(0, 0, q, fa[0], fb[0]);
 
-    // W: the registers hold stage kt + 1, to be written to slot s ^ 1; Lq:
-    // afterwards they are loaded with stage kt + 2; P (last stage): they are
-    // loaded with the next tile's stage 0.  W and Lq are compile-time, so the
-    // k-steps carry no branches.
     auto stage = [&](int kt, auto w_tag, auto l_tag) {
       constexpr bool W = decltype(w_tag)::value, Lq = decltype(l_tag)::value;
       constexpr bool LAST = !W && !Lq;
@@ -1047,27 +1031,26 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int cur = ks & 1, nxt = cur ^ 1;
-        wait_lgkmcnt<0>();  // this k-step's fragments and the earlier LDS writes have landed
-        if (ks == KS - 1 && W) barrier_lds();  // stage kt + 1 is visible; slot s is free
+        wait_lgkmcnt<0>();
+        if (ks == KS - 1 && W) barrier_lds();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < NMF; ++t) {
           const int i = t / FN, j = t % FN;
           asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fb[cur][j]), "v"(fa[cur][i]));
           __builtin_amdgcn_sched_barrier(0);
-          // the next k-step's fragments, one read after each of the first 8 MFMAs
+          // the next k-step's six fragments, one after each of the first six MFMAs
           if (t < FM + FN) {
             if (ks + 1 < KS) read_one(s, ks + 1, t, fa[nxt], fb[nxt]);
             else if (W) read_one(s ^ 1, 0, t, fa[nxt], fb[nxt]);
           }
-          // writes of the staged stage kt + 1: registers 0-7 in k-step 0,
-          // 8-15 in k-step 1; a register is reloaded after its write: 0-5 in
-          // k-step 1, 6-10 in k-step 2, 11-15 in k-step 3
-          if (W && ks < 2 && (t & 1) == 0) swrite(s ^ 1, ks * 8 + t / 2);
+          // writes of the staged stage kt + 1: registers 0-3 in k-step 0,
+          // 4-7 in k-step 1; reloaded after their write: 0-3 in k-step 1,
+          // 4-7 in k-step 2
+          if (W && ks < 2 && (t & 1) == 0) swrite(s ^ 1, ks * 4 + t / 2);
           int l = -1;
-          if (ks == 1 && (t & 1) == 1 && t / 2 < 6) l = t / 2;
-          if (ks == 2 && t % 3 == 0 && t / 3 < 5) l = 6 + t / 3;
-          if (ks == 3 && t % 3 == 0 && t / 3 < 5) l = 11 + t / 3;
+          if (ks == 1 && (t & 1) == 1) l = t / 2;
+          if (ks == 2 && (t & 1) == 1) l = 4 + t / 2;
           if (l >= 0) {
             if constexpr (Lq) gload(it, kt + 2, l);
             if constexpr (LAST) {
@@ -1088,14 +1071,10 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
     }
     stage(kt, T0{}, T0{});
 
-    // the last MFMAs wrote the accumulators behind the compiler's back: wait
-    // out the MFMA-write -> AGPR-read hazard
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     if (it.part != nullptr) {
-      // split-K slice: raw accumulators in 16-byte groups, group-major so
-      // consecutive threads store consecutive 16 bytes
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1109,8 +1088,11 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
           }
       return;
     }
-    __syncthreads();  // every wave is done reading the k-stages in LDS
-    w4_epilogue<EPI>(a, acc, it.g, it.rows, it.row0, it.n0, wm, wn, lr, lk, lane, smem + wave * (128 * 256));
+    __syncthreads();
+    {
+      const int ln = threadIdx.x & 63;  // recomputed here: not kept live through the main loop
+      w8_epilogue<EPI>(a, acc, it.g, it.rows, it.row0, it.n0, wm, wn, ln & 31, ln >> 5, ln, smem + wave * (128 * 128));
+    }
   };
 
   int k = 0;
@@ -1118,56 +1100,11 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_bf16_w4_kernel(const Gemm
   bool have = next_item(k, cur), pre = false;
   while (have) {
     const bool has_next = next_item(k, nit);
-    run_tile(cur, pre, has_next, nit);  // one call site keeps the tile body inlined once
+    run_tile(cur, pre, has_next, nit);
     pre = has_next;
     cur = nit;
     have = has_next;
   }
-}
-
-// Second pass of the four-wave kernel's tail split, one single-wave
-// workgroup per 32-row strip of each 128 x 128 block of a tail tile: the
-// reduction is bound by load latency, so spreading a tile over sixteen
-// compute units shortens it.  Workgroup xcd + 8 (16 tau + 4 q + i) takes
-// strip i (accumulator row i) of block q (wave q of the GEMM, wm = q / 2,
-// wn = q % 2) of tail tile tau: it reads exactly the sums that wave wrote
-// for that strip, adds the slices in slice order and runs the same epilogue
-// on the strip, so the output is that of a whole-tile fixup.
-template <int EPI>
-__global__ void __launch_bounds__(64) grouped_gemm_w4_fixup_kernel(const GemmArgs a) {
-  constexpr int BM = 256, BN = 256, NT = 256, MF = 32, FN = 4, NACC = 16;
-  constexpr int QS = FN * NACC / 4;  // 16-byte groups of one strip per thread
-  const int lane = threadIdx.x;
-  const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3, tau = r >> 4, q = (r >> 2) & 3, i = r & 3;
-  const int nx = (a.grid - xcd + 7) >> 3;
-  if (a.partial == nullptr || a.K / 64 < 16) return;
-  const int m_used = rows_tiles_used<BM>(a);
-  const TailPlan tp = tail_plan((int64_t)m_used * a.n_tiles, xcd, nx, true);
-  if (tp.split == 0 || tau >= tp.tail) return;
-  int64_t row0;
-  int n0, g, rows;
-  if (!tile_coords<BM, BN, w4_band(EPI)>(a, m_used, tp.full_end + tau, row0, n0, g, rows)) return;
-  const int wm = q >> 1, wn = q & 1;
-  if (wm * 128 + i * MF >= rows) return;  // strip wholly past the rows: nothing to store
-  const int tid = q * 64 + lane;  // the GEMM thread whose sums these are
-  float4 sum[QS];
-#pragma unroll
-  for (int k = 0; k < QS; ++k) sum[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  // the GEMM stored group k of accumulator (i, j) as group (i FN + j) NACC / 4 + k
-  const float* part0 = a.partial + (size_t)(xcd + 8 * tau * tp.split) * (BM * BN);
-  fixup_add_slices<QS>(sum, part0 + ((size_t)(i * QS) * NT + tid) * 4, (size_t)NT * 4, (size_t)8 * (BM * BN),
-                       tp.split);
-  f32x16_t acc[1][FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int v = 0; v < NACC / 4; ++v) {
-      const float4 u = sum[j * (NACC / 4) + v];
-      acc[0][j][4 * v] = u.x; acc[0][j][4 * v + 1] = u.y; acc[0][j][4 * v + 2] = u.z; acc[0][j][4 * v + 3] = u.w;
-    }
-  // the strip as a one-fragment wave tile: its rows start at (4 wm + i) * 32
-  gemm_epilogue<BN, 2, 2, false, EPI, MF, 1, FN, NACC, false, false>(a, acc, g, rows, row0, n0, 4 * wm + i, wn,
-                                                                      lane % MF, lane / MF);
 }
 
 // fp32 activations and weights: vector-ALU tiles (64 x 64 outputs, 4 x 4 per
@@ -1305,10 +1242,11 @@ hipError_t run_bf16(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial
   return hipGetLastError();
 }
 
-// The four-wave 256 x 256 kernel: one workgroup per CU (it holds all 512
-// registers of each SIMD's one wave), split-K tail as above.
+// The eight-wave 256 x 256 kernel: one workgroup per CU (128 KB of LDS), the
+// general kernel's split-K fixup for its tail.  lda == ldb: the two operands
+// share their load offsets (both rows hold the K contraction values).
 template <int EPI>
-hipError_t run_bf16_w4(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial_bytes) {
+hipError_t run_bf16_w8(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t partial_bytes) {
   a.m_tiles = (int)ceil_div(rows_cap, 256);
   a.n_tiles = a.N / 256;
   const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
@@ -1318,12 +1256,12 @@ hipError_t run_bf16_w4(GemmArgs a, int64_t rows_cap, hipStream_t st, size_t part
   grid = grid < 8 ? 8 : grid / 8 * 8;
   a.grid = (int)grid;
   if (a.partial != nullptr && (size_t)grid * 256 * 256 * sizeof(float) > partial_bytes) a.partial = nullptr;
-  if (a.a_rows != nullptr) return hipErrorInvalidValue;  // no rows read in place here
-  hipLaunchKernelGGL(grouped_gemm_bf16_w4_kernel<EPI>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  if (a.a_rows != nullptr || a.lda != a.ldb) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(grouped_gemm_bf16_w8_kernel<EPI>, dim3((unsigned)grid), dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partial == nullptr) return e;
-  // the fixup: sixteen single-wave workgroups per possible tail tile
-  hipLaunchKernelGGL(grouped_gemm_w4_fixup_kernel<EPI>, dim3((unsigned)grid * 16), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((grouped_gemm_fixup_kernel<256, 256, 64, 2, 4, 2, false, EPI, kW8Band, 32, false>),
+                     dim3((unsigned)grid * 8), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1341,12 +1279,12 @@ static hipError_t run_f32(GemmArgs a, int64_t rows_cap, hipStream_t st) {
 // multiples of 64, so the wider variants fall back when needed.
 // Whether the up product of problem p (N = d_ff, K = d) runs on a kernel
 // that reads rows in place (a_rows): the choices of run_regime and
-// run_regime_a8 below, minus the four-wave kernel and the 256 x 256 tiles of
+// run_regime_a8 below, minus the eight-wave kernel and the 256 x 256 tiles of
 // the general one (their launchers refuse a_rows), and the fp32 kernel.
 bool expert_up_reads_in_place(const Problem& p) {
   if (p.act != DT_BF16) return false;
   if (p.act_quant || gemm_regime(p) != 0) return true;
-  return p.d_ff % 256 != 0;  // prefill: 256 x 256 tiles (four-wave for bf16 weights) unless N % 256 != 0
+  return p.d_ff % 256 != 0;  // prefill: 256 x 256 tiles (eight-wave for bf16 weights) unless N % 256 != 0
 }
 
 template <bool BFP8, int EPI>
@@ -1354,7 +1292,7 @@ static hipError_t run_regime(int regime, const GemmArgs& a, int64_t rows_cap, hi
   const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0, k128 = a.K % 128 == 0;
   switch (regime) {
     case 0:
-      if (!BFP8 && n256 && a.K % 64 == 0) return run_bf16_w4<EPI>(a, rows_cap, st, pb);
+      if (!BFP8 && n256 && a.K % 64 == 0) return run_bf16_w8<EPI>(a, rows_cap, st, pb);
       if (n256) return run_bf16<256, 256, 64, 4, 2, 2, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);
       if (n128) return run_bf16<256, 128, 64, 4, 2, 3, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);
       return run_bf16<256, 64, 64, 4, 1, 3, BFP8, EPI, -4, 32>(a, rows_cap, st, pb);

@@ -4,7 +4,7 @@ With one expert whose W1 is the identity (d = d_ff = 256) and b1 = 0, the
 pre-activation of h[r][j] is exactly x[r][j] (one product by 1.0, the rest
 by 0.0, summed in float32), so h = GeLU(x) as each epilogue evaluates it,
 rounded once to the activation type.  Every kernel family with a GeLU
-epilogue is reached: the four-wave 256 x 256 kernel (bf16, 256+ rows per
+epilogue is reached: the eight-wave 256 x 256 kernel (bf16, 256+ rows per
 expert), the general kernel's 256-row tiles (fp8 weights), its 128-row tiles
 (64-255 rows) and 16-row tiles (under 64 rows), and the float32 kernel.
 Checked against x Phi(x) = x/2 erfc(-x / sqrt 2) in float64 (scipy's erfc,

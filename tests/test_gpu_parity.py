@@ -432,7 +432,7 @@ def test_empty_batch_noop():
 LAYER_VS_STAGES = [
     ("decode", None),                                                           # 16-row tiles, rows in place
     ("dsv3_fp8", None),                                                         # 128-row fp8 tiles, in place
-    ("mixtral_prefill", None),                                                  # four-wave kernel, gathered rows
+    ("mixtral_prefill", None),                                                  # eight-wave kernel, gathered rows
     ("mid_bf16", dict(S=600, d=512, d_ff=768, E=8, K=2)),                       # 128-row bf16 tiles, in place
     ("prefill_n128", dict(S=2048, d=512, d_ff=640, E=8, K=2)),                  # 256 x 128 tiles, in place
 ]
