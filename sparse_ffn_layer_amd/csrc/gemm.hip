@@ -1058,11 +1058,15 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_bf16_w8_kernel(const Gemm
               else if (W) read_one(s ^ 1, 0, t, fa[nxt], fb[nxt]);
             }
             // writes of the staged stage kt + 1: registers 0-3 in k-step 0,
-            // 4-7 in k-step 1; reloaded after their write: 0-3 in k-step 1,
-            // 4-7 in k-step 2
+            // 4-7 in k-step 1; reloaded after their write: 0-3 in k-step 0,
+            // one slot after each write, 4-7 in k-step 2 (loads take the
+            // longest lead that fits: reloading 4-7 in k-step 1 spills,
+            // spreading the reloads two per k-step over all four k-steps
+            // cut their lead and cost 11 %; this order, against 0-3 in
+            // k-step 1: Mixtral expert_down 0.827-0.829 -> 0.820 ms)
             if (W && ks < 2 && (t & 1) == 0) swrite(s ^ 1, ks * 4 + t / 2);
             int l = -1;
-            if (ks == 1 && (t & 1) == 1) l = t / 2;
+            if (ks == 0 && (t & 1) == 1) l = t / 2;
             if (ks == 2 && (t & 1) == 1) l = 4 + t / 2;
             if (l >= 0) {
               if constexpr (Lq) gload(it, kt + 2, l);
